@@ -1,0 +1,343 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+Kinds of pin used here: number-format definitions checked against an
+independent library cast and against a table from the OCP FP8 specification;
+exact rational arithmetic (fractions) for the K mean and for fma; brute-force
+integer dot products for the scores; closed forms (two-pass softmax attention
+in float64, online == two-pass when quantization is off); invariants (K
+smoothing leaves softmax unchanged, scale equivariance, permutation
+equivariance); special cases with known answers (one key, constant K).
+"""
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sage_oracle as so
+from quantized_exact_attention_amd.synth import WORKLOADS, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+def bf16_exact(shape, rng, scale=1.0):
+    """float32 array of values exactly representable in bfloat16."""
+    t = torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def softmax_attention_f64(q, k, v, sm_scale):
+    """Textbook softmax(Q K^T * scale) V in float64 (two passes, stable)."""
+    s = (q.astype(np.float64) @ k.astype(np.float64).T) * float(sm_scale)
+    s -= s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return (p @ v.astype(np.float64)) / p.sum(axis=1, keepdims=True)
+
+
+# ---------------------------------------------------------------- formats ---
+
+def test_e4m3_golden_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "e4m3_ocp_values.txt")) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            val, code = line.split()[:2]
+            rows.append((float(val), int(code, 16)))
+    x = f32([r[0] for r in rows])
+    got = so.e4m3_encode(x)
+    assert [int(c) for c in got] == [r[1] for r in rows]
+    # decoding the code gives back the rounded value
+    dec = so.e4m3_decode(got)
+    assert dec[0] == 0.0 and np.signbit(dec[1])
+
+
+def test_e4m3_encode_matches_torch_cast_dense_sweep():
+    # every 97th float32 bit pattern in [0, 463.99], both signs, plus all
+    # midpoints between adjacent E4M3 values and their float32 neighbours
+    hi = np.float32(463.99).view(np.uint32)
+    bits = np.arange(0, int(hi), 97, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    vals = so.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1000))])
+    x = np.concatenate([x, -x])
+    ours = so.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_e4m3_decode_all_codes_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = so.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    both_nan = np.isnan(ours) & np.isnan(ref)
+    assert np.all(both_nan | (ours == ref))
+    assert np.isnan(ours).sum() == 2
+
+
+def test_e4m3_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        so.e4m3_encode(f32([464.0]))
+
+
+def test_bf16_rne_matches_torch_cast():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(200000) * np.exp2(rng.integers(-30, 30, 200000))).astype(np.float32)
+    # exact ties: low 16 bits == 0x8000, both parities of the kept part
+    ties = (rng.integers(0x00800000, 0x7F000000, 20000, dtype=np.uint32) & 0xFFFF0000) | 0x8000
+    x = np.concatenate([x, ties.view(np.float32), -ties.view(np.float32)])
+    ours = so.bf16_bits_rne(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def _round_fraction_to_f32(fr: Fraction) -> np.float32:
+    cand = np.float32(float(fr))
+    best = None
+    for c in (np.nextafter(cand, np.float32(-np.inf)), cand, np.nextafter(cand, np.float32(np.inf))):
+        dist = abs(Fraction(float(c)) - fr)
+        key = (dist, int(np.float32(c).view(np.uint32)) & 1)   # ties: even mantissa
+        if best is None or key < best[0]:
+            best = (key, c)
+    return np.float32(best[1])
+
+
+def test_fma_f32_exact_rational():
+    rng = np.random.default_rng(2)
+    a = f32(rng.standard_normal(3000))
+    b = f32(rng.standard_normal(3000))
+    c = f32(rng.standard_normal(3000) * np.exp2(rng.integers(-40, 5, 3000)))
+    # constructed halfway cases: (1+2^-12)^2 = 1 + 2^-11 + 2^-24 is a float32 tie
+    a = np.concatenate([a, f32([1 + 2**-12] * 3)])
+    b = np.concatenate([b, f32([1 + 2**-12] * 3)])
+    c = np.concatenate([c, f32([0.0, 2.0**-60, -(2.0**-60)])])
+    got = so.fma_f32(a, b, c)
+    for ai, bi, ci, gi in zip(a, b, c, got):
+        exact = Fraction(float(ai)) * Fraction(float(bi)) + Fraction(float(ci))
+        assert gi == _round_fraction_to_f32(exact), (ai, bi, ci)
+    assert got[-3] == np.float32(1 + 2**-11)            # tie to even
+    assert got[-2] == np.float32(1 + 2**-11 + 2**-23)   # just above the tie
+    assert got[-1] == np.float32(1 + 2**-11)            # just below the tie
+
+
+# ------------------------------------------------------------ quant stages --
+
+def test_k_mean_exact_rational():
+    rng = np.random.default_rng(3)
+    k = bf16_exact((37, 8), rng, 3.0) + bf16_exact((1, 8), rng, 2.0)
+    k = torch.from_numpy(k.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    ksum, mean = so.k_channel_mean(k)
+    for c in range(8):
+        exact = sum(Fraction(float(x)) for x in k[:, c])
+        assert Fraction(float(ksum[c])) == exact
+        # float64 quotient rounded to float32 equals the correctly rounded mean here
+        assert mean[c] == _round_fraction_to_f32(exact / 37)
+
+
+def test_int8_block_quant_bounds_and_invariants():
+    rng = np.random.default_rng(4)
+    x = bf16_exact((300, 64), rng)
+    x[5, 3] = 40.0  # outlier in block 0
+    codes, scales = so.quantize_int8_blocks(x, 128)
+    assert codes.shape == (384, 64) and scales.shape == (3,)
+    assert np.all(codes[300:] == 0)
+    for g in range(3):
+        blk = x[g * 128:min(300, (g + 1) * 128)]
+        amax = np.abs(blk).max()
+        assert scales[g] == np.float32(amax) / np.float32(127)
+        cb = codes[g * 128:g * 128 + blk.shape[0]].astype(np.int64)
+        assert np.abs(cb).max() == 127                      # the absmax element maps to +-127
+        # code is the nearest integer to x*127/A up to float32 rounding of the factor
+        exact = blk.astype(np.float64) * 127.0 / float(amax)
+        assert np.all(np.abs(exact - cb) <= 0.5 + 1e-5)
+        assert np.all(np.sign(cb) * np.sign(blk) >= 0)
+    # all-zero block: scale 0, codes 0
+    z = np.zeros((64, 8), np.float32)
+    c0, s0 = so.quantize_int8_blocks(z, 64)
+    assert s0[0] == 0 and np.all(c0 == 0)
+
+
+def test_v_fp8_channel_quant():
+    rng = np.random.default_rng(5)
+    v = bf16_exact((100, 16), rng)
+    v[:, 7] = 0.0
+    codes, vs, vamax = so.quantize_v_channels(v, 128)
+    assert codes.shape == (128, 16) and np.all(codes[100:] == 0)
+    assert vs[7] == 0 and np.all(codes[:, 7] == 0)
+    for c in range(16):
+        if c == 7:
+            continue
+        dec = so.e4m3_decode(codes[:100, c]) * (float(vamax[c]) / 448.0)
+        # E4M3 relative spacing is 2^-3 in the normal range: error <= half a step
+        rel = np.abs(dec - v[:, c]) / np.maximum(np.abs(v[:, c]), 2.0**-6 * float(vamax[c]) / 448)
+        assert rel.max() <= 2.0**-4 * (1 + 1e-6)
+        i = np.argmax(np.abs(v[:, c]))
+        assert codes[i, c] & 0x7F == 0x7E                   # channel max maps to 448
+
+
+# ----------------------------------------------------- attention pipeline --
+
+def _tiny(nq, nkv, d, seed, bias=True, outlier=0.0):
+    rng = np.random.default_rng(seed)
+    q = bf16_exact((nq, d), rng)
+    k = bf16_exact((nkv, d), rng) + (bf16_exact((1, d), rng, 2.0) if bias else 0)
+    v = bf16_exact((nkv, d), rng)
+    if outlier:
+        q[rng.random((nq, d)) < outlier] *= 20
+        k[rng.random((nkv, d)) < outlier] *= 20
+    to = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    return to(q), to(k), to(v)
+
+
+@pytest.mark.parametrize("nq,nkv,d", [(5, 7, 64), (130, 65, 64), (129, 200, 128)])
+def test_scores_brute_force_int(nq, nkv, d):
+    q, k, v = _tiny(nq, nkv, d, 10 + nq)
+    p = so.prep_bh(q, k, v)
+    rows = np.array([0, nq // 2, nq - 1])
+    _, ck = so.attention_rows(p, rows, want_checkpoints=True)
+    for ri, i in enumerate(rows):
+        for t in range(0, nkv, 3):
+            ref = sum(int(p.q_codes[i, c]) * int(p.k_codes[t, c]) for c in range(d))
+            assert ck.S[ri, t] == ref
+    # pad keys: zero codes give zero scores, masked to P8 = 0
+    T = -(-nkv // 64)
+    assert np.all(ck.P8[:, nkv:T * 64] == 0)
+
+
+@pytest.mark.parametrize("nq,nkv,d", [(7, 1, 64), (64, 64, 64), (130, 200, 128), (33, 333, 64)])
+def test_online_equals_two_pass_without_quantization(nq, nkv, d):
+    q, k, v = _tiny(nq, nkv, d, 20 + nkv)
+    p = so.prep_bh(q, k, v)
+    sm = so.default_sm_scale(d)
+    ob = so.attention_rows(p, None, sm, quant_qk=False, quant_p=False, quant_v=False, q_f32=q)
+    got = so.bf16_bits_to_f32(ob).astype(np.float64)
+    ref = softmax_attention_f64(q, k, v, float(sm))
+    # float32 rounding of scores/p/RO plus one bf16 rounding of the output
+    assert np.allclose(got, ref, rtol=2**-8, atol=1e-5)
+
+
+def test_k_smoothing_invariance_f64():
+    q, k, v = _tiny(40, 150, 64, 31)
+    sm = float(so.default_sm_scale(64))
+    mean = k.astype(np.float64).mean(axis=0)
+    a = softmax_attention_f64(q, k, v, sm)
+    b = softmax_attention_f64(q, k - mean, v, sm)
+    assert np.abs(a - b).max() < 1e-12
+    # and the oracle's unquantized path, which scores against smoothed K, agrees
+    p = so.prep_bh(q, k, v)
+    o = so.bf16_bits_to_f32(so.attention_rows(p, None, quant_qk=False, quant_p=False,
+                                              quant_v=False, q_f32=q))
+    assert np.allclose(o, a, rtol=2**-8, atol=1e-5)
+
+
+@pytest.mark.parametrize("nq,nkv,d,outlier,bound", [
+    (128, 192, 128, 0.0, 0.999), (100, 300, 64, 0.0, 0.999), (300, 1000, 128, 0.0, 0.999),
+    # x20 outliers set the per-block INT8 scale, so ordinary entries keep only a
+    # few bits: the method itself loses accuracy there (bound is not a pin)
+    (64, 128, 128, 0.03, 0.95)])
+def test_quantized_pipeline_cosine_vs_f64(nq, nkv, d, outlier, bound):
+    q, k, v = _tiny(nq, nkv, d, 40 + nkv, outlier=outlier)
+    p = so.prep_bh(q, k, v)
+    o = so.bf16_bits_to_f32(so.attention_rows(p)).astype(np.float64).ravel()
+    ref = softmax_attention_f64(q, k, v, float(so.default_sm_scale(d))).ravel()
+    cos = o @ ref / np.linalg.norm(o) / np.linalg.norm(ref)
+    assert cos >= bound, cos
+
+
+def test_online_softmax_invariants():
+    q, k, v = _tiny(50, 400, 64, 51)
+    p = so.prep_bh(q, k, v)
+    _, ck = so.attention_rows(p, want_checkpoints=True)
+    T = ck.m.shape[1]
+    assert np.all(np.diff(ck.m, axis=1) >= 0)                 # running max never decreases
+    assert np.all(ck.alpha[:, 0] == 0)                         # first tile: nothing to rescale
+    assert np.all((ck.alpha >= 0) & (ck.alpha <= 1))
+    same = ck.m[:, 1:] == ck.m[:, :-1]
+    assert np.all(ck.alpha[:, 1:][same] == 1)
+    # after the tile holding the row maximum, d >= 1 (that key contributes p = 1)
+    jmax = np.argmax(ck.m == ck.m[:, -1:], axis=1)
+    for i in range(50):
+        assert np.all(ck.d[i, jmax[i]:] >= 1)
+    # the key attaining the running max of its tile gets P8 = 448 where m rose
+    for i in range(50):
+        for j in range(T):
+            if j == 0 or ck.m[i, j] > ck.m[i, j - 1]:
+                assert (ck.P8[i, j * 64:(j + 1) * 64] == 0x7E).any()
+
+
+def test_single_key_special_case():
+    q, k, v = _tiny(9, 1, 64, 61)
+    p = so.prep_bh(q, k, v)
+    o = so.bf16_bits_to_f32(so.attention_rows(p))
+    # one key: p = 1, P8 = 448, d = 1, O = bf16(dec(v8) * v_scale) for every row
+    deq = (so.e4m3_decode(p.v_codes[0]) * p.v_scale.astype(np.float64)).astype(np.float32)
+    for i in range(9):
+        assert np.allclose(o[i], deq, rtol=2**-7, atol=0)
+
+
+def test_constant_k_special_case():
+    rng = np.random.default_rng(71)
+    q = bf16_exact((20, 64), rng)
+    krow = bf16_exact((1, 64), rng)
+    k = np.repeat(krow, 90, axis=0)
+    v = bf16_exact((90, 64), rng)
+    p = so.prep_bh(q, k, v)
+    assert np.all(p.k_codes == 0) and np.all(p.k_scale == 0)
+    O, ck = so.attention_rows(p, want_checkpoints=True)
+    assert np.all(ck.S == 0)
+    assert np.all(ck.P8[:, :90] == 0x7E) and np.all(ck.P8[:, 90:] == 0)
+    mean_deq = (so.e4m3_decode(p.v_codes[:90]) * p.v_scale.astype(np.float64)).mean(axis=0)
+    assert np.allclose(so.bf16_bits_to_f32(O)[0], mean_deq, rtol=2**-7, atol=1e-6)
+
+
+def test_scale_and_permutation_equivariance():
+    q, k, v = _tiny(128, 130, 64, 81)
+    base = so.bf16_bits_to_f32(so.attention_rows(so.prep_bh(q, k, v)))
+    # V * 2 -> O * 2 exactly (the per-channel scale absorbs the factor)
+    o2 = so.bf16_bits_to_f32(so.attention_rows(so.prep_bh(q, k, v * 2)))
+    assert np.array_equal(o2, base * 2)
+    # joint permutation of channels of Q, K, V permutes O's channels
+    perm = np.random.default_rng(1).permutation(64)
+    op = so.bf16_bits_to_f32(so.attention_rows(so.prep_bh(q[:, perm], k[:, perm], v[:, perm])))
+    assert np.array_equal(op, base[:, perm])
+    # permuting query rows inside one 128-row block permutes O's rows
+    rp = np.random.default_rng(2).permutation(128)
+    orow = so.bf16_bits_to_f32(so.attention_rows(so.prep_bh(q[rp], k, v)))
+    assert np.array_equal(orow, base[rp])
+
+
+def test_kv_tile_order_matters_for_p8():
+    """Strict tile order is observable: reversing K/V rows changes P8 codes."""
+    q, k, v = _tiny(16, 256, 64, 91)
+    _, a = so.attention_rows(so.prep_bh(q, k, v), want_checkpoints=True)
+    _, b = so.attention_rows(so.prep_bh(q, k[::-1].copy(), v[::-1].copy()), want_checkpoints=True)
+    assert not np.array_equal(a.P8[:, :256], b.P8[:, ::-1][:, :256])
+
+
+def test_workload_inputs_reproducible_and_shaped():
+    w = WORKLOADS["ragged_tails"]
+    q1, k1, v1 = make_inputs(w, B=1, H=2, Nq=50, Nkv=60)
+    q2, k2, v2 = make_inputs(w, B=1, H=2, Nq=50, Nkv=60)
+    assert torch.equal(q1, q2) and torch.equal(k1, k2) and torch.equal(v1, v2)
+    assert q1.dtype == torch.bfloat16 and q1.shape == (1, 2, 50, 128)
+    # K carries a per-channel bias of standard deviation about 2
+    assert float(k1.float().mean(dim=2).std()) > 1.0
+
+
+def test_single_tile_workload_end_to_end():
+    w = WORKLOADS["single_tile"]
+    q, k, v = (t[0, 0].float().numpy() for t in make_inputs(w))
+    p = so.prep_bh(q, k, v)
+    O, ck = so.attention_rows(p, want_checkpoints=True)
+    assert O.shape == (128, 128) and ck.S.shape == (128, 192) and ck.m.shape == (128, 3)
+    ref = softmax_attention_f64(q, k, v, float(so.default_sm_scale(128)))
+    o = so.bf16_bits_to_f32(O).astype(np.float64)
+    cos = (o.ravel() @ ref.ravel()) / np.linalg.norm(o) / np.linalg.norm(ref)
+    assert cos >= 0.999
