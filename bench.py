@@ -1,0 +1,189 @@
+"""Benchmark of the quantized attention hot path (prep + fused forward) on one GPU.
+
+One step = sage_quant_prep + sage_attn_fwd over one batch of seeded synthetic
+bf16 inputs already resident in HBM.  Prints ONE JSON line:
+  value       effective TFLOPS = 4*B*H*Nq*Nkv*D / (ms_per_step) (whole step)
+  roofline    the fused forward kernel against the dense INT8/FP8 matrix peak,
+              timed with HIP events on the stream it is launched on
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+Default workload: the long video-token sequence (B=1, H=24, N=32760, D=128).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense INT8 (POP/s) and FP8 (FLOP/s) peak, 5.0 P
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("sage_fwd.hip", "sage_common.h"):
+        with open(os.path.join(ROOT, "quantized_exact_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per forward launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """Time the oracle on a bounded sample and scale to effective TFLOPS.
+
+    Sample: the prep of head (0,0) plus as many 128-row Q blocks of that head
+    as fit in the budget; the full-workload time is extrapolated linearly
+    (prep per head x B*H, attention per block x B*H*ceil(Nq/128)).
+    """
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import sage_oracle as so
+
+    with threadpool_limits(limits=1):
+        qh, kh, vh = (t[0, 0].float().numpy() for t in (q, k, v))
+        t0 = time.perf_counter()
+        p = so.prep_bh(qh, kh, vh)
+        t_prep = time.perf_counter() - t0
+        nqb = -(-w.Nq // 128)
+        blocks = 0
+        t_att = 0.0
+        rng = np.random.default_rng(0)
+        order = rng.permutation(nqb)
+        while t_att < budget_s and blocks < nqb:
+            qb = int(order[blocks])
+            rows = np.arange(qb * 128, min(w.Nq, qb * 128 + 128))
+            t0 = time.perf_counter()
+            so.attention_rows(p, rows)
+            t_att += time.perf_counter() - t0
+            blocks += 1
+    BH = w.B * w.H
+    t_total = t_prep * BH + (t_att / blocks) * BH * nqb
+    return {
+        "value": w.flops / t_total / 1e12,
+        "unit": "TFLOPS",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "prep of 1 of %d heads (%.2f s) + %d of %d 128-row Q blocks of that head (%.2f s), "
+                  "extrapolated linearly to the whole workload (%.0f s)" % (BH, t_prep, blocks, BH * nqb,
+                                                                           t_att, t_total),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_video")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention to time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from quantized_exact_attention_amd import build as qbuild
+    from quantized_exact_attention_amd import sage
+    from quantized_exact_attention_amd.synth import WORKLOADS, make_inputs
+
+    if not os.path.exists(qbuild.LIB_PATH):
+        qbuild.build()
+    w = WORKLOADS[args.workload]
+    print("bench: generating %s inputs B=%d H=%d Nq=%d Nkv=%d D=%d" % (w.name, w.B, w.H, w.Nq, w.Nkv, w.D),
+          file=sys.stderr, flush=True)
+    q, k, v = make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    quant = sage.sage_quant_prep(qd, kd, vd)
+    out = sage.sage_attn_fwd(quant)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        sage.sage_quant_prep(qd, kd, vd, out=quant)
+        sage.sage_attn_fwd(quant, out=out)
+    torch.cuda.synchronize()
+    print("bench: warmup done, timing %d steps" % args.steps, file=sys.stderr, flush=True)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        sage.sage_quant_prep(qd, kd, vd, out=quant)
+        ev[i][1].record(stream)
+        sage.sage_attn_fwd(quant, out=out)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
+    prep_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    fwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    fwd_avg = statistics.mean(fwd_ms)
+    achieved = w.flops / (fwd_avg * 1e-3) / 1e12
+
+    res = {
+        "metric": "effective attention TFLOPS (4*B*H*Nq*Nkv*D/t) and % of INT8/FP8 MFMA peak",
+        "value": w.flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "D": w.D,
+                   "causal": False, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": 100.0 * (w.flops / (ms_per_step * 1e-3) / 1e12) / MFMA_PEAK_TFLOPS,
+        "step_ms_p50": statistics.median(step_ms),
+        "step_ms_cv": statistics.pstdev(step_ms) / statistics.mean(step_ms),
+        "prep_ms_p50": statistics.median(prep_ms),
+        "fwd_ms_p50": statistics.median(fwd_ms),
+        "fwd_tflops_p50": w.flops / (statistics.median(fwd_ms) * 1e-3) / 1e12,
+        "roofline": {
+            "kernel": "k_attn_fwd<%d,false>" % w.D,
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / MFMA_PEAK_TFLOPS,
+            "traffic": measured_traffic(w.name),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

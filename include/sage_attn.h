@@ -1,0 +1,167 @@
+/*
+ * sage_attn.h - C ABI of the MI355X (gfx950) SageAttention2-style quantized
+ * exact attention forward: INT8 QK^T with int32 accumulation, online softmax
+ * with FP8 (OCP E4M3FN) probabilities, FP8 PV with two-level accumulation and
+ * BF16 output.
+ *
+ * The operation is the numerical contract named in "Experiment Log", Phase 0
+ * Import And Verification (stage list: Q/K preparation, K smoothing, INT8
+ * quantization, QK traversal, online softmax, FP8 V/P, two-level PV
+ * accumulation, final conversion, ragged tails) with the invariants of the
+ * Phase 1 State-Ownership Decision (strict KV-tile order, exact FP8 score
+ * bytes, per-tile RO rescaling, two-level PV, final conversion).
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers on the current HIP device; the
+ *    caller allocates and frees every buffer.  The library never allocates,
+ *    never synchronizes and keeps no per-call state: calls are asynchronous on
+ *    `stream` (a hipStream_t; NULL = the default stream) and inputs must stay
+ *    unchanged until the stream has passed the call.
+ *  - Validation is pure host code and runs before any HIP call.  The return
+ *    value is SAGE_OK or a negative SAGE_E_* status; nothing is printed and
+ *    nothing aborts.  Device faults surface at the caller's next sync.
+ *  - Shapes: B, H >= 1; Nq, Nkv >= 1; D in {64, 128}.  Inputs Q [B,H,Nq,D],
+ *    K and V [B,H,Nkv,D] and output O [B,H,Nq,D] are bfloat16 with element
+ *    strides (b, h, n) given in sage_strides_t; the d dimension is contiguous.
+ *    Strides must be multiples of 8 elements and base pointers 16-byte aligned.
+ *  - Calls that share buffers on one stream are ordered; calls on different
+ *    streams that write the same buffers race.
+ */
+#ifndef SAGE_ATTN_H
+#define SAGE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define SAGE_OK 0
+#define SAGE_E_NULL (-1)     /* a required pointer is NULL */
+#define SAGE_E_SHAPE (-2)    /* B, H, Nq or Nkv out of range */
+#define SAGE_E_HEADDIM (-3)  /* D not 64 or 128 */
+#define SAGE_E_ALIGN (-4)    /* base pointer or stride misaligned */
+#define SAGE_E_ALIAS (-5)    /* the output overlaps an input or a code buffer */
+#define SAGE_E_DEVICE (-6)   /* no device, or the device is not gfx950 */
+#define SAGE_E_LAUNCH (-7)   /* a kernel launch failed (hipGetLastError) */
+#define SAGE_E_ARG (-8)      /* another argument is invalid */
+
+/* problem shape */
+typedef struct sage_shape {
+  int32_t B, H, Nq, Nkv, D;
+} sage_shape_t;
+
+/* element strides of dims (b, h, n) for each bf16 tensor; d is contiguous */
+typedef struct sage_strides {
+  int64_t q[3], k[3], v[3], o[3];
+} sage_strides_t;
+
+/*
+ * Quantized operands written by sage_quant_prep and read by sage_attn_fwd.
+ * Sizes come from sage_buffer_bytes().  Let NQB = ceil(Nq/128),
+ * T = ceil(Nkv/64).  Pad rows (queries >= Nq, keys >= Nkv) hold code 0.
+ *
+ *  q_codes  int8, per (b,h): NQB*128 rows in groups of 32 rows; a group is
+ *           stored as [D/32 steps][64 lanes][16 bytes]: lane L, step s holds
+ *           row 32g + L%32, channels 32s + 16*(L/32) ... +15.  This is the
+ *           operand order of the 32x32x32 INT8 matrix instruction.
+ *  q_scale  float [B,H,NQB]: absmax/127 of each 128-row block (0 if all zero).
+ *  k_codes  int8, per (b,h): T*64 rows of smoothed K in the same 32-row-group
+ *           layout as q_codes (a 64-key tile is two consecutive groups).
+ *  k_scale  float [B,H,T]: absmax/127 of each 64-row block of smoothed K.
+ *  v_codes  uint8 OCP E4M3FN, per (b,h) and 64-key tile:
+ *           [D/32 blocks][2 halves][64 lanes][16 bytes]: block c, half h,
+ *           lane L, byte e holds V[key = 32h + 8*(e/4) + 4*(L/32) + e%4]
+ *           [channel = 32c + L%32] quantized with the channel scale.
+ *  v_scale  float [B,H,D]: per-channel absmax/448 over all Nkv keys.
+ *  k_mean   float [B,H,D]: per-channel mean of K over all Nkv keys.
+ *  workspace  scratch for the prep statistics (sage_buffer_bytes).
+ */
+typedef struct sage_quant {
+  int8_t *q_codes;
+  float *q_scale;
+  int8_t *k_codes;
+  float *k_scale;
+  uint8_t *v_codes;
+  float *v_scale;
+  float *k_mean;
+  void *workspace;
+} sage_quant_t;
+
+enum sage_buffer {
+  SAGE_BUF_Q_CODES = 0,
+  SAGE_BUF_Q_SCALE = 1,
+  SAGE_BUF_K_CODES = 2,
+  SAGE_BUF_K_SCALE = 3,
+  SAGE_BUF_V_CODES = 4,
+  SAGE_BUF_V_SCALE = 5,
+  SAGE_BUF_K_MEAN = 6,
+  SAGE_BUF_WORKSPACE = 7,
+  SAGE_BUF_COUNT = 8
+};
+
+/* Size in bytes of buffer `which` (enum sage_buffer) for `shape`.
+ * Returns SAGE_OK, SAGE_E_NULL, SAGE_E_SHAPE, SAGE_E_HEADDIM or SAGE_E_ARG. */
+int sage_buffer_bytes(const sage_shape_t *shape, int which, size_t *bytes);
+
+/*
+ * Stages 1-2 of the contract ("Experiment Log", Phase 0 stage list: Q/K
+ * preparation, K smoothing, INT8 quantization, FP8 V):
+ *   k_mean[c] = fp32(exact sum_t K[t,c] / Nkv)           (FP64 sum, exact)
+ *   K smoothed: ks = fp32(K - k_mean)
+ *   Q per 128-row block, ks per 64-row block: A = max|x|, scale = fp32(A/127),
+ *     code = RNE(fp32(x * fp32(127/A))) in [-127, 127]; A = 0 -> all zero
+ *   V per channel: v_scale = fp32(vamax/448), code = E4M3FN_RNE(fp32(v * fp32(448/vamax)))
+ * q, k, v: bf16 device tensors with strides->q/k/v.  Writes every buffer of
+ * `quant` (including the workspace).  Launches 5 kernels on `stream`.
+ */
+int sage_quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *shape,
+                    const sage_strides_t *strides, const sage_quant_t *quant, void *stream);
+
+/*
+ * Stages 3-5 ("Experiment Log", Phase 0 stage list and Phase 1 invariants;
+ * checkpoint names of Phase 2B Fixed Aligned Numerical Prototype):
+ * for each query row, 64-key tiles j = 0..T-1 strictly in order:
+ *   S = q_codes . k_codes_j^T                     (INT8 MFMA, int32, exact)
+ *   s = S * fp32(fp32(q_scale * k_scale_j) * sm_scale * log2 e); keys >= Nkv masked
+ *   m' = max(m, max s); alpha = 2^(m - m'); p = 2^(s - m')
+ *   d = d * alpha + sum p                         (from FP32 p)
+ *   P8 = E4M3FN(448 p)                            ("exact FP8 score bytes")
+ *   partial = P8 . V8_j (FP8 MFMA, FP32); RO = RO * alpha + partial
+ * then O = bf16(RO / d * v_scale / 448), rows < Nq stored.
+ * sm_scale <= 0 selects 1/sqrt(D).  out: bf16 [B,H,Nq,D] with strides->o; it
+ * must not overlap any buffer of `quant`.  One kernel launch on `stream`.
+ */
+int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *shape, float sm_scale, void *out,
+                  const sage_strides_t *strides, void *stream);
+
+/*
+ * Diagnostic variant of sage_attn_fwd (same kernel source, capture build):
+ * runs only the n_units work units listed in `units` (device int32 array;
+ * unit = ((b*H + h) * NQB + qblock)) and, besides their O rows, writes the
+ * checkpoints of the Phase 2B prototype description for them:
+ *   s_cap   int32 [n_units][128][T*64]   QK scores (pad keys: the raw score)
+ *   p8_cap  uint8 [n_units][128][T*64]   FP8 probability codes (masked: 0)
+ *   md_cap  float [n_units][128][T][2]   running max m and 448*d after tile j
+ * Rows >= Nq of a unit hold values for zero pad codes.  Unit ids must be
+ * distinct; the kernel skips ids outside [0, B*H*NQB) and their capture slots
+ * are left unwritten.
+ */
+int sage_attn_fwd_capture(const sage_quant_t *quant, const sage_shape_t *shape, float sm_scale,
+                          void *out, const sage_strides_t *strides, const int32_t *units,
+                          int32_t n_units, int32_t *s_cap, uint8_t *p8_cap, float *md_cap,
+                          void *stream);
+
+/* SAGE_OK if `device` is a gfx950 GPU, else SAGE_E_DEVICE (one HIP query). */
+int sage_device_check(int device);
+
+/* Static description of a status code. */
+const char *sage_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_ATTN_H */

@@ -1,0 +1,244 @@
+// C ABI of the gfx950 quantized attention library: argument validation (pure
+// host code, before any HIP call), buffer sizing and kernel launches.
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/sage_attn.h"
+#include "sage_common.h"
+
+using namespace sage;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+int check_shape(const sage_shape_t *s) {
+  if (!s) return SAGE_E_NULL;
+  if (s->D != 64 && s->D != 128) return SAGE_E_HEADDIM;
+  if (s->B < 1 || s->H < 1 || s->Nq < 1 || s->Nkv < 1) return SAGE_E_SHAPE;
+  const int64_t BH = (int64_t)s->B * s->H;
+  if (BH > 65535) return SAGE_E_SHAPE;                      // second grid dimension of the prep
+  if ((int64_t)s->Nq > (1 << 28) || (int64_t)s->Nkv > (1 << 28)) return SAGE_E_SHAPE;
+  if (BH * ceil_div(s->Nq, kBQ) > INT32_MAX / 2) return SAGE_E_SHAPE;
+  return SAGE_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_strides(const int64_t st[3]) {
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0 || (st[i] & 7) != 0) return SAGE_E_ALIGN;
+  return SAGE_OK;
+}
+
+// bytes spanned by a strided bf16 tensor [B,H,N,D]
+size_t span_bytes(const sage_shape_t *s, const int64_t st[3], int N) {
+  return (size_t)(((int64_t)(s->B - 1) * st[0] + (int64_t)(s->H - 1) * st[1] +
+                   (int64_t)(N - 1) * st[2] + s->D) * 2);
+}
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+size_t buffer_bytes(const sage_shape_t *s, int which) {
+  const size_t BH = (size_t)s->B * s->H;
+  const size_t nqb = ceil_div(s->Nq, kBQ), T = ceil_div(s->Nkv, kBK);
+  const int nchunk = ceil_div(s->Nkv, kStatChunk);
+  switch (which) {
+    case SAGE_BUF_Q_CODES: return BH * nqb * kBQ * s->D;
+    case SAGE_BUF_Q_SCALE: return BH * nqb * sizeof(float);
+    case SAGE_BUF_K_CODES: return BH * T * kBK * s->D;
+    case SAGE_BUF_K_SCALE: return BH * T * sizeof(float);
+    case SAGE_BUF_V_CODES: return BH * T * kBK * s->D;
+    case SAGE_BUF_V_SCALE: return BH * s->D * sizeof(float);
+    case SAGE_BUF_K_MEAN: return BH * s->D * sizeof(float);
+    case SAGE_BUF_WORKSPACE:
+      return align256(ws_ksum_bytes((int)BH, nchunk, s->D)) + align256(ws_vmax_bytes((int)BH, nchunk, s->D)) +
+             align256(ws_vinv_bytes((int)BH, s->D));
+    default: return 0;
+  }
+}
+
+int check_quant(const sage_quant_t *q) {
+  if (!q || !q->q_codes || !q->q_scale || !q->k_codes || !q->k_scale || !q->v_codes || !q->v_scale ||
+      !q->k_mean || !q->workspace)
+    return SAGE_E_NULL;
+  if (!aligned16(q->q_codes) || !aligned16(q->k_codes) || !aligned16(q->v_codes) || !aligned16(q->workspace) ||
+      ((uintptr_t)q->q_scale & 3) || ((uintptr_t)q->k_scale & 3) || ((uintptr_t)q->v_scale & 3) ||
+      ((uintptr_t)q->k_mean & 3))
+    return SAGE_E_ALIGN;
+  return SAGE_OK;
+}
+
+// true if [p, p+n) overlaps any buffer of the quant set
+bool overlaps_quant(const void *p, size_t n, const sage_quant_t *q, const sage_shape_t *s) {
+  const void *bufs[SAGE_BUF_COUNT] = {q->q_codes, q->q_scale, q->k_codes, q->k_scale,
+                                      q->v_codes, q->v_scale, q->k_mean, q->workspace};
+  for (int i = 0; i < SAGE_BUF_COUNT; ++i)
+    if (overlap(p, n, bufs[i], buffer_bytes(s, i))) return true;
+  return false;
+}
+
+int device_ok() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SAGE_E_DEVICE;
+  return sage_device_check(dev);
+}
+
+float resolve_sl2(float sm_scale, int D) {
+  const float sm = sm_scale > 0.f ? sm_scale : (float)(1.0 / std::sqrt((double)D));
+  return sm * 1.44269504088896340736f;   // fp32(sm_scale * fp32(log2 e))
+}
+
+int fill_fwd(const sage_quant_t *q, const sage_shape_t *s, float sm_scale, void *out, const sage_strides_t *st,
+             FwdParams *fp) {
+  int r = check_shape(s);
+  if (r) return r;
+  if (!out || !st) return SAGE_E_NULL;
+  if ((r = check_quant(q))) return r;
+  if (!aligned16(out) || check_strides(st->o)) return SAGE_E_ALIGN;
+  if (!std::isfinite(sm_scale)) return SAGE_E_ARG;
+  if (overlaps_quant(out, span_bytes(s, st->o, s->Nq), q, s)) return SAGE_E_ALIAS;
+  std::memset(fp, 0, sizeof(*fp));
+  fp->q_codes = q->q_codes;
+  fp->q_scale = q->q_scale;
+  fp->k_codes = q->k_codes;
+  fp->k_scale = q->k_scale;
+  fp->v_codes = q->v_codes;
+  fp->v_scale = q->v_scale;
+  fp->out = (uint16_t *)out;
+  for (int i = 0; i < 3; ++i) fp->os[i] = st->o[i];
+  fp->H = s->H;
+  fp->Nq = s->Nq;
+  fp->Nkv = s->Nkv;
+  fp->nqb = ceil_div(s->Nq, kBQ);
+  fp->T = ceil_div(s->Nkv, kBK);
+  fp->n_units = s->B * s->H * fp->nqb;
+  fp->sl2 = resolve_sl2(sm_scale, s->D);
+  return SAGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sage_status_string(int status) {
+  switch (status) {
+    case SAGE_OK: return "ok";
+    case SAGE_E_NULL: return "a required pointer is NULL";
+    case SAGE_E_SHAPE: return "shape out of range (B, H, Nq, Nkv >= 1; B*H <= 65535)";
+    case SAGE_E_HEADDIM: return "head dimension must be 64 or 128";
+    case SAGE_E_ALIGN: return "base pointer not 16-byte aligned or stride not a multiple of 8 elements";
+    case SAGE_E_ALIAS: return "output overlaps an input or a quantized buffer";
+    case SAGE_E_DEVICE: return "no HIP device, or the device is not gfx950";
+    case SAGE_E_LAUNCH: return "kernel launch failed";
+    case SAGE_E_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int sage_device_check(int device) {
+  if (device < 0 || device >= kMaxDevices) return SAGE_E_DEVICE;
+  int known = g_device_ok[device].load(std::memory_order_relaxed);
+  if (known == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return SAGE_E_DEVICE;
+    known = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_device_ok[device].store(known, std::memory_order_relaxed);
+  }
+  return known == 1 ? SAGE_OK : SAGE_E_DEVICE;
+}
+
+int sage_buffer_bytes(const sage_shape_t *shape, int which, size_t *bytes) {
+  if (!bytes) return SAGE_E_NULL;
+  const int r = check_shape(shape);
+  if (r) return r;
+  if (which < 0 || which >= SAGE_BUF_COUNT) return SAGE_E_ARG;
+  *bytes = buffer_bytes(shape, which);
+  return SAGE_OK;
+}
+
+int sage_quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *s,
+                    const sage_strides_t *st, const sage_quant_t *quant, void *stream) {
+  int r = check_shape(s);
+  if (r) return r;
+  if (!q || !k || !v || !st) return SAGE_E_NULL;
+  if ((r = check_quant(quant))) return r;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || check_strides(st->q) || check_strides(st->k) ||
+      check_strides(st->v))
+    return SAGE_E_ALIGN;
+  if (overlaps_quant(q, span_bytes(s, st->q, s->Nq), quant, s) ||
+      overlaps_quant(k, span_bytes(s, st->k, s->Nkv), quant, s) ||
+      overlaps_quant(v, span_bytes(s, st->v, s->Nkv), quant, s))
+    return SAGE_E_ALIAS;
+  if ((r = device_ok())) return r;
+
+  PrepParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = (const uint16_t *)q;
+  p.k = (const uint16_t *)k;
+  p.v = (const uint16_t *)v;
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = st->q[i];
+    p.ks[i] = st->k[i];
+    p.vs[i] = st->v[i];
+  }
+  p.B = s->B;
+  p.H = s->H;
+  p.Nq = s->Nq;
+  p.Nkv = s->Nkv;
+  p.D = s->D;
+  p.nqb = ceil_div(s->Nq, kBQ);
+  p.T = ceil_div(s->Nkv, kBK);
+  p.nchunk = ceil_div(s->Nkv, kStatChunk);
+  p.q_codes = quant->q_codes;
+  p.q_scale = quant->q_scale;
+  p.k_codes = quant->k_codes;
+  p.k_scale = quant->k_scale;
+  p.v_codes = quant->v_codes;
+  p.v_scale = quant->v_scale;
+  p.k_mean = quant->k_mean;
+  const int BH = s->B * s->H;
+  uint8_t *ws = (uint8_t *)quant->workspace;
+  p.ws_ksum = (double *)ws;
+  ws += align256(ws_ksum_bytes(BH, p.nchunk, s->D));
+  p.ws_vmax = (float *)ws;
+  ws += align256(ws_vmax_bytes(BH, p.nchunk, s->D));
+  p.ws_vinv = (float *)ws;
+  return launch_prep(p, (hipStream_t)stream) == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
+}
+
+int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *s, float sm_scale, void *out,
+                  const sage_strides_t *st, void *stream) {
+  FwdParams fp;
+  int r = fill_fwd(quant, s, sm_scale, out, st, &fp);
+  if (r) return r;
+  if ((r = device_ok())) return r;
+  return launch_fwd(fp, s->D, fp.n_units, false, (hipStream_t)stream) == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
+}
+
+int sage_attn_fwd_capture(const sage_quant_t *quant, const sage_shape_t *s, float sm_scale, void *out,
+                          const sage_strides_t *st, const int32_t *units, int32_t n_units, int32_t *s_cap,
+                          uint8_t *p8_cap, float *md_cap, void *stream) {
+  FwdParams fp;
+  int r = fill_fwd(quant, s, sm_scale, out, st, &fp);
+  if (r) return r;
+  if (!units || !s_cap || !p8_cap || !md_cap) return SAGE_E_NULL;
+  if (n_units < 1 || n_units > fp.n_units) return SAGE_E_ARG;
+  if (!aligned16(s_cap) || !aligned16(p8_cap) || !aligned16(md_cap)) return SAGE_E_ALIGN;
+  if ((r = device_ok())) return r;
+  fp.units = units;
+  fp.s_cap = s_cap;
+  fp.p8_cap = p8_cap;
+  fp.md_cap = md_cap;
+  return launch_fwd(fp, s->D, n_units, true, (hipStream_t)stream) == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
+}
+
+}  // extern "C"

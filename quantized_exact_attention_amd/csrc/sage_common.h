@@ -1,0 +1,66 @@
+// Shared definitions of the gfx950 HIP path (kernels and host launchers).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Block sizes of the contract: Q quantization block / workgroup query tile,
+// and the K quantization block == online-softmax KV tile (two 8 KiB K/V slots
+// of 64 one-byte rows at D = 128, "Experiment Log", Phase 2A capability decision).
+constexpr int kBQ = 128;
+constexpr int kBK = 64;
+constexpr int kStatChunk = 512;   // keys per block of the K/V statistics pass
+
+struct PrepParams {
+  const uint16_t *q, *k, *v;      // bf16 bits
+  int64_t qs[3], ks[3], vs[3];    // element strides (b, h, n)
+  int B, H, Nq, Nkv, D;
+  int nqb, T, nchunk;
+  int8_t *q_codes;
+  float *q_scale;
+  int8_t *k_codes;
+  float *k_scale;
+  uint8_t *v_codes;
+  float *v_scale;
+  float *k_mean;
+  double *ws_ksum;                // [B*H][nchunk][D]
+  float *ws_vmax;                 // [B*H][nchunk][D]
+  float *ws_vinv;                 // [B*H][D]
+};
+
+struct FwdParams {
+  const int8_t *q_codes;
+  const float *q_scale;
+  const int8_t *k_codes;
+  const float *k_scale;
+  const uint8_t *v_codes;
+  const float *v_scale;
+  uint16_t *out;                  // bf16 bits
+  int64_t os[3];
+  int H, Nq, Nkv, nqb, T;
+  int n_units;                    // B*H*nqb
+  float sl2;                      // fp32(sm_scale * fp32(log2 e))
+  // capture build only
+  const int32_t *units;
+  int32_t *s_cap;
+  uint8_t *p8_cap;
+  float *md_cap;
+};
+
+// Workspace layout of the prep statistics, shared by the size query and the launcher.
+inline size_t ws_ksum_bytes(int BH, int nchunk, int D) { return (size_t)BH * nchunk * D * sizeof(double); }
+inline size_t ws_vmax_bytes(int BH, int nchunk, int D) { return (size_t)BH * nchunk * D * sizeof(float); }
+inline size_t ws_vinv_bytes(int BH, int D) { return (size_t)BH * D * sizeof(float); }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+hipError_t launch_prep(const PrepParams &p, hipStream_t stream);
+hipError_t launch_fwd(const FwdParams &p, int D, int grid, bool capture, hipStream_t stream);
+
+}  // namespace sage

@@ -1,0 +1,224 @@
+"""Python binding of the gfx950 quantized attention library (ctypes).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libsage_attn.so``.  PyTorch provides device memory (``torch.empty``) and the
+stream (``torch.cuda.current_stream()``).  There is no fallback: if the
+library is not built, or a call fails, an exception is raised.
+
+Names mirror the C ABI in ``include/sage_attn.h``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+from .build import LIB_PATH
+
+SAGE_OK = 0
+BQ = 128
+BK = 64
+BUFFERS = ["q_codes", "q_scale", "k_codes", "k_scale", "v_codes", "v_scale", "k_mean", "workspace"]
+
+_STATUS = {
+    0: "SAGE_OK", -1: "SAGE_E_NULL", -2: "SAGE_E_SHAPE", -3: "SAGE_E_HEADDIM", -4: "SAGE_E_ALIGN",
+    -5: "SAGE_E_ALIAS", -6: "SAGE_E_DEVICE", -7: "SAGE_E_LAUNCH", -8: "SAGE_E_ARG",
+}
+
+
+class SageError(RuntimeError):
+    def __init__(self, status: int, what: str, text: str):
+        super().__init__("%s failed: %s (%s)" % (what, _STATUS.get(status, status), text))
+        self.status = status
+
+
+class SageShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Nq", ctypes.c_int32),
+                ("Nkv", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
+class SageStrides(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_int64 * 3), ("k", ctypes.c_int64 * 3),
+                ("v", ctypes.c_int64 * 3), ("o", ctypes.c_int64 * 3)]
+
+
+class SageQuantC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BUFFERS]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libsage_attn.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+        L.sage_buffer_bytes.argtypes = [ctypes.POINTER(SageShape), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+        L.sage_quant_prep.argtypes = [vp, vp, vp, ctypes.POINTER(SageShape), ctypes.POINTER(SageStrides),
+                                      ctypes.POINTER(SageQuantC), vp]
+        L.sage_attn_fwd.argtypes = [ctypes.POINTER(SageQuantC), ctypes.POINTER(SageShape), f32, vp,
+                                    ctypes.POINTER(SageStrides), vp]
+        L.sage_attn_fwd_capture.argtypes = [ctypes.POINTER(SageQuantC), ctypes.POINTER(SageShape), f32, vp,
+                                            ctypes.POINTER(SageStrides), vp, i32, vp, vp, vp, vp]
+        L.sage_device_check.argtypes = [ctypes.c_int]
+        L.sage_status_string.argtypes = [ctypes.c_int]
+        L.sage_status_string.restype = ctypes.c_char_p
+        for name in ("sage_buffer_bytes", "sage_quant_prep", "sage_attn_fwd", "sage_attn_fwd_capture",
+                     "sage_device_check"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != SAGE_OK:
+        raise SageError(status, what, lib().sage_status_string(status).decode())
+
+
+def status_string(status: int) -> str:
+    return lib().sage_status_string(status).decode()
+
+
+def sage_buffer_bytes(B: int, H: int, Nq: int, Nkv: int, D: int, which: int) -> int:
+    n = ctypes.c_size_t(0)
+    shape = SageShape(B, H, Nq, Nkv, D)
+    _check(lib().sage_buffer_bytes(ctypes.byref(shape), which, ctypes.byref(n)), "sage_buffer_bytes")
+    return n.value
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _strides3(t: torch.Tensor):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B,H,N,D] tensor with a contiguous last dimension")
+    return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+@dataclass
+class SageQuant:
+    """Device buffers of the quantized operands (see sage_quant_t in the header)."""
+    B: int
+    H: int
+    Nq: int
+    Nkv: int
+    D: int
+    q_codes: torch.Tensor
+    q_scale: torch.Tensor
+    k_codes: torch.Tensor
+    k_scale: torch.Tensor
+    v_codes: torch.Tensor
+    v_scale: torch.Tensor
+    k_mean: torch.Tensor
+    workspace: torch.Tensor
+
+    @property
+    def shape(self) -> SageShape:
+        return SageShape(self.B, self.H, self.Nq, self.Nkv, self.D)
+
+    @property
+    def nqb(self) -> int:
+        return -(-self.Nq // BQ)
+
+    @property
+    def T(self) -> int:
+        return -(-self.Nkv // BK)
+
+    def c_struct(self) -> SageQuantC:
+        return SageQuantC(*[getattr(self, n).data_ptr() for n in BUFFERS])
+
+    @classmethod
+    def allocate(cls, B, H, Nq, Nkv, D, device) -> "SageQuant":
+        dt = {"q_codes": torch.int8, "k_codes": torch.int8, "v_codes": torch.uint8, "workspace": torch.uint8}
+        bufs = {}
+        for i, name in enumerate(BUFFERS):
+            nbytes = sage_buffer_bytes(B, H, Nq, Nkv, D, i)
+            dtype = dt.get(name, torch.float32)
+            count = nbytes // torch.empty(0, dtype=dtype).element_size()
+            bufs[name] = torch.empty(count, dtype=dtype, device=device)
+        return cls(B, H, Nq, Nkv, D, **bufs)
+
+
+def sage_quant_prep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: SageQuant | None = None,
+                    stream=None) -> SageQuant:
+    """K mean, K smoothing, INT8 Q/K per block and FP8 V per channel on the GPU."""
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("q, k, v must be bfloat16 CUDA tensors")
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if k.shape != (B, H, Nkv, D) or v.shape != (B, H, Nkv, D):
+        raise ValueError("k and v must be [B,H,Nkv,D] matching q")
+    quant = out if out is not None else SageQuant.allocate(B, H, Nq, Nkv, D, q.device)
+    st = SageStrides()
+    st.q, st.k, st.v = _strides3(q), _strides3(k), _strides3(v)
+    qc = quant.c_struct()
+    _check(lib().sage_quant_prep(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(quant.shape),
+                                 ctypes.byref(st), ctypes.byref(qc), _stream_handle(stream)), "sage_quant_prep")
+    return quant
+
+
+def _out_tensor(quant: SageQuant, out):
+    if out is None:
+        out = torch.empty(quant.B, quant.H, quant.Nq, quant.D, dtype=torch.bfloat16, device=quant.q_codes.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (quant.B, quant.H, quant.Nq, quant.D):
+        raise ValueError("out must be bfloat16 [B,H,Nq,D]")
+    return out
+
+
+def sage_attn_fwd(quant: SageQuant, sm_scale: float | None = None, out: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """Fused INT8-QK / FP8-PV online-softmax attention; returns bf16 [B,H,Nq,D]."""
+    out = _out_tensor(quant, out)
+    st = SageStrides()
+    st.o = _strides3(out)
+    qc = quant.c_struct()
+    _check(lib().sage_attn_fwd(ctypes.byref(qc), ctypes.byref(quant.shape),
+                               ctypes.c_float(0.0 if sm_scale is None else sm_scale), out.data_ptr(),
+                               ctypes.byref(st), _stream_handle(stream)), "sage_attn_fwd")
+    return out
+
+
+def sage_attn_fwd_capture(quant: SageQuant, units, sm_scale: float | None = None,
+                          out: torch.Tensor | None = None, stream=None):
+    """Run the listed work units with checkpoint capture.
+
+    Returns (out, s_cap int32 [n,128,T*64], p8_cap uint8 [n,128,T*64],
+    md_cap float32 [n,128,T,2]) as device tensors.
+    """
+    out = _out_tensor(quant, out)
+    dev = quant.q_codes.device
+    units_t = torch.as_tensor(list(units), dtype=torch.int32).to(dev)
+    n = units_t.numel()
+    T = quant.T
+    s_cap = torch.zeros(n, BQ, T * BK, dtype=torch.int32, device=dev)
+    p8_cap = torch.zeros(n, BQ, T * BK, dtype=torch.uint8, device=dev)
+    md_cap = torch.zeros(n, BQ, T, 2, dtype=torch.float32, device=dev)
+    st = SageStrides()
+    st.o = _strides3(out)
+    qc = quant.c_struct()
+    _check(lib().sage_attn_fwd_capture(ctypes.byref(qc), ctypes.byref(quant.shape),
+                                       ctypes.c_float(0.0 if sm_scale is None else sm_scale), out.data_ptr(),
+                                       ctypes.byref(st), units_t.data_ptr(), n, s_cap.data_ptr(),
+                                       p8_cap.data_ptr(), md_cap.data_ptr(), _stream_handle(stream)),
+           "sage_attn_fwd_capture")
+    return out, s_cap, p8_cap, md_cap
+
+
+def sage_attention(q, k, v, sm_scale: float | None = None) -> torch.Tensor:
+    """Both calls of the hot path: prep then fused forward."""
+    return sage_attn_fwd(sage_quant_prep(q, k, v), sm_scale)
+
+
+def default_sm_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

@@ -1,0 +1,122 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/sage_attn.h, sizes buffers, and rejects bad arguments with
+the documented status before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_exact_attention_amd import build as qbuild
+from quantized_exact_attention_amd import sage
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qbuild.LIB_PATH):
+        qbuild.build()
+    return sage.lib()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "sage_attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_\w+)\s*\(", text)))
+
+
+def test_exports_every_header_function(L):
+    names = header_functions()
+    assert {"sage_quant_prep", "sage_attn_fwd", "sage_attn_fwd_capture", "sage_buffer_bytes",
+            "sage_status_string", "sage_device_check"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for st in range(-8, 1):
+        assert sage.status_string(st) not in ("", "unknown status")
+    assert sage.status_string(-99) == "unknown status"
+
+
+def test_buffer_bytes_formulas(L):
+    B, H, Nq, Nkv, D = 2, 3, 1000, 333, 128
+    nqb, T = 8, 6
+    expect = [B * H * nqb * 128 * D, B * H * nqb * 4, B * H * T * 64 * D, B * H * T * 4,
+              B * H * T * 64 * D, B * H * D * 4, B * H * D * 4]
+    for which, e in enumerate(expect):
+        assert sage.sage_buffer_bytes(B, H, Nq, Nkv, D, which) == e
+    assert sage.sage_buffer_bytes(B, H, Nq, Nkv, D, 7) > 0
+
+
+@pytest.mark.parametrize("shape,status", [
+    ((1, 1, 128, 64, 96), -3), ((1, 1, 0, 64, 64), -2), ((1, 1, 64, 0, 64), -2),
+    ((0, 1, 64, 64, 64), -2), ((300, 300, 64, 64, 64), -2)])
+def test_buffer_bytes_rejects_bad_shapes(L, shape, status):
+    n = ctypes.c_size_t()
+    s = sage.SageShape(*shape)
+    assert L.sage_buffer_bytes(ctypes.byref(s), 0, ctypes.byref(n)) == status
+    assert L.sage_buffer_bytes(None, 0, ctypes.byref(n)) == -1
+    assert L.sage_buffer_bytes(ctypes.byref(sage.SageShape(1, 1, 8, 8, 64)), 9, ctypes.byref(n)) == -8
+
+
+def _fake_quant(base=1 << 40, step=1 << 30):
+    q = sage.SageQuantC(*[base + i * step for i in range(8)])
+    return q
+
+
+def _strides(B, H, N, D):
+    st = sage.SageStrides()
+    for f in ("q", "k", "v", "o"):
+        getattr(st, f)[:] = [H * N * D, N * D, D]
+    return st
+
+
+def test_prep_validation_before_any_hip_call(L):
+    shape = sage.SageShape(1, 2, 100, 100, 64)
+    st = _strides(1, 2, 100, 64)
+    qc = _fake_quant()
+    q, k, v = 1 << 36, 2 << 36, 3 << 36
+    call = lambda *a: L.sage_quant_prep(*a)
+    assert call(q, k, v, None, ctypes.byref(st), ctypes.byref(qc), None) == -1
+    assert call(None, k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(qc), None) == -1
+    assert call(q, k, v, ctypes.byref(shape), ctypes.byref(st), None, None) == -1
+    assert call(q + 2, k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(qc), None) == -4
+    bad = _strides(1, 2, 100, 64)
+    bad.k[2] = 68
+    assert call(q, k, v, ctypes.byref(shape), ctypes.byref(bad), ctypes.byref(qc), None) == -4
+    alias = _fake_quant(base=q)  # q_codes starts where q does
+    assert call(q, k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(alias), None) == -5
+    d96 = sage.SageShape(1, 2, 100, 100, 96)
+    assert call(q, k, v, ctypes.byref(d96), ctypes.byref(st), ctypes.byref(qc), None) == -3
+
+
+def test_fwd_validation_before_any_hip_call(L):
+    shape = sage.SageShape(2, 2, 300, 77, 128)
+    st = _strides(2, 2, 300, 128)
+    qc = _fake_quant()
+    out = 1 << 36
+    f = L.sage_attn_fwd
+    assert f(None, ctypes.byref(shape), 0.0, out, ctypes.byref(st), None) == -1
+    assert f(ctypes.byref(qc), ctypes.byref(shape), 0.0, None, ctypes.byref(st), None) == -1
+    assert f(ctypes.byref(qc), ctypes.byref(shape), 0.0, out + 8, ctypes.byref(st), None) == -4
+    assert f(ctypes.byref(qc), ctypes.byref(shape), float("nan"), out, ctypes.byref(st), None) == -8
+    # output overlapping the K codes buffer
+    assert f(ctypes.byref(qc), ctypes.byref(shape), 0.0, qc.k_codes + 4096, ctypes.byref(st), None) == -5
+    nulls = _fake_quant()
+    nulls.v_scale = None
+    assert f(ctypes.byref(nulls), ctypes.byref(shape), 0.0, out, ctypes.byref(st), None) == -1
+    cap = L.sage_attn_fwd_capture
+    assert cap(ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(st), None, 1,
+               1 << 37, 1 << 38, 1 << 39, None) == -1
+    assert cap(ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(st), 1 << 35, 0,
+               1 << 37, 1 << 38, 1 << 39, None) == -8
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(sage, "_lib", None)
+    monkeypatch.setattr(sage, "LIB_PATH", "/nonexistent/libsage_attn.so")
+    with pytest.raises(RuntimeError):
+        sage.lib()
