@@ -1,8 +1,8 @@
 """Build the gfx950 HIP library in-tree: quantized_exact_attention_amd/lib/libsage_attn.so.
 
 Every source is compiled for gfx950 only, with FP contraction off (the kernels
-call fma explicitly where they want one) and packed-FP32 instruction selection
-disabled.
+call fma explicitly where they want one), packed-FP32 instruction selection
+disabled and matrix-instruction results kept in VGPRs.
 """
 
 from __future__ import annotations
@@ -22,6 +22,9 @@ SOURCES = ["sage_prep.hip", "sage_fwd.hip", "sage_abi.hip"]
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-instruction accumulators in VGPRs: the softmax and the RO update
+    # read them directly instead of copying every value out of AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
 ]
 
