@@ -19,9 +19,9 @@
 //   B-operand layout of O^T = V^T . P^T (no LDS round trip for P)
 //   partial^T[D x 32] = V_j^T . P8^T         (D/32) v_mfma_f32_32x32x64_f8f6f4
 //   RO = fma(RO, alpha, partial)            (two-level accumulation)
-// K and V tiles (operand-ordered by the prep stage) are streamed through a
-// double-buffered LDS ring: the next tile's global loads are issued before the
-// current tile's math and written to the other buffer after it.
+// K and V tiles (operand-ordered by the prep stage) are streamed through two
+// LDS buffers by global_load_lds (HBM -> LDS without registers): the copy of
+// tile j+1 is issued before tile j's math and waited for at its end.
 #include <climits>
 
 #include "sage_common.h"
@@ -49,15 +49,177 @@ __device__ __forceinline__ float partner_sum(float x) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// Three 4-wave workgroups per CU (3 waves per SIMD): the register budget is
+// 168 VGPRs per lane, which the per-wave state (RO 64, S/p 32, P8 8, Q 16,
+// partial 16-64) fits.
+constexpr int kFwdBlocksPerCU = 3;
+
 // log2(448): P is produced directly as 448 * 2^(s - m) = 2^(s - m + log2 448).
 constexpr float kLog2_448 = 8.80735492205760410744f;
 
+// Read-only scalars through the constant address space: a scalar (SMEM) load,
+// tracked by lgkmcnt, so waiting for it never waits for the in-flight K/V DMA.
+__device__ __forceinline__ float load_uniform(const float *ptr) {
+  return *(const __attribute__((address_space(4))) float *)ptr;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Issue the HBM -> LDS copy of K/V tile t (global_load_lds_dwordx4, no VGPRs):
+// wave w copies 1 KiB chunks c = i*4 + w of the [K tile | V tile] image.
+template <int D>
+__device__ __forceinline__ void issue_tile(uint8_t *dst, const int8_t *kg, const uint8_t *vg, int t, int wave,
+                                           int lane) {
+  constexpr int TILE = kBK * D;
+  constexpr int NLD = 2 * TILE / 4096;
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int c = i * 4 + wave;
+    const uint8_t *src = i < NLD / 2 ? (const uint8_t *)kg + (size_t)t * TILE + c * 1024
+                                     : vg + (size_t)t * TILE + (c - TILE / 1024) * 1024;
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(src + lane * 16), (lds_void_t *)(dst + c * 1024), 16, 0, 0);
+  }
+}
+
+template <int D>
+struct FwdState {
+  float m, dsum;
+  v16f ro[D / 32];
+};
+
+// One 64-key tile of the ordered traversal for one wavefront (32 query rows).
+// `cur` holds tile j; tile j+1 is copied into `nxt` meanwhile.  Ends with the
+// workgroup barrier that publishes `nxt` and retires `cur`.
 template <int D, bool CAP>
-__global__ __launch_bounds__(256) void k_attn_fwd(FwdParams p) {
+__device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, const v4i *qop, float sq, int j,
+                                          const uint8_t *cur, uint8_t *nxt, const int8_t *kg, const uint8_t *vg,
+                                          const float *ksc, int wave, int lane, int row) {
+  constexpr int NS = D / 32;
+  constexpr int TILE = kBK * D;
+  const int T = p.T;
+  const int hi = lane >> 5;   // which 4-key group of each 8 this lane holds
+  if (j + 1 < T) issue_tile<D>(nxt, kg, vg, j + 1, wave, lane);
+  const uint8_t *kl = cur;
+  const uint8_t *vl = cur + TILE;
+
+  // ---- S^T = K_j . Q^T (int32, exact) ----
+  v16i sacc[2];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const v4i a = *(const v4i *)(kl + (kb * NS + s) * 1024 + lane * 16);
+      sacc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[s], s == 0 ? (v16i){} : sacc[kb], 0, 0, 0);
+    }
+  }
+  if (CAP) {
+    int32_t *sc = p.s_cap + ((size_t)blockIdx.x * kBQ + row) * ((size_t)T * kBK) + (size_t)j * kBK;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sc[kb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3)] = sacc[kb][v];
+  }
+  // ragged tail: keys >= Nkv of the last tile take no part in max, sum or PV
+  const int kvalid = p.Nkv - j * kBK;
+  const bool masked = kvalid < kBK;
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (kb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3) >= kvalid) sacc[kb][v] = INT_MIN;
+  }
+
+  // ---- online softmax; max in the integer domain (the per-tile factor is >= 0) ----
+  int mx8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int kb = i >> 2, v0 = 4 * (i & 3);
+    mx8[i] = max(max(sacc[kb][v0], sacc[kb][v0 + 1]), max(sacc[kb][v0 + 2], sacc[kb][v0 + 3]));
+  }
+  int mx = max(max(max(mx8[0], mx8[1]), max(mx8[2], mx8[3])), max(max(mx8[4], mx8[5]), max(mx8[6], mx8[7])));
+  mx = partner_max(mx);
+  const float c = (sq * load_uniform(ksc + j)) * p.sl2;   // fp32(fp32(sq * sk_j) * sl2)
+  const float mnew = fmaxf(st.m, (float)mx * c);
+  const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);   // "rescale"; 0 on the first tile
+  const float nb = kLog2_448 - mnew;
+  float pv[2][16];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) pv[kb][v] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sacc[kb][v], c, nb));
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (kb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3) >= kvalid) pv[kb][v] = 0.f;
+  }
+  // row sum as a tree (short dependency chains)
+  float s8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int kb = i >> 2, v0 = 4 * (i & 3);
+    s8[i] = (pv[kb][v0] + pv[kb][v0 + 1]) + (pv[kb][v0 + 2] + pv[kb][v0 + 3]);
+  }
+  float ls = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+  ls = partner_sum(ls);
+  st.dsum = __builtin_fmaf(st.dsum, alpha, ls);      // d carries the factor 448
+  st.m = mnew;
+
+  // ---- P8 (E4M3FN, RNE) packed straight into the B operand of the PV product ----
+  v8i pop;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int kb = w >> 2, v0 = 4 * (w & 3);
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(pv[kb][v0], pv[kb][v0 + 1], 0, false);
+    x = __builtin_amdgcn_cvt_pk_fp8_f32(pv[kb][v0 + 2], pv[kb][v0 + 3], x, true);
+    pop[w] = x;
+  }
+  if (CAP) {
+    uint8_t *pc = p.p8_cap + ((size_t)blockIdx.x * kBQ + row) * ((size_t)T * kBK) + (size_t)j * kBK;
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * (w & 3) + e;
+        pc[(w >> 2) * 32 + 8 * (v >> 2) + 4 * hi + (v & 3)] = (uint8_t)((uint32_t)pop[w] >> (8 * e));
+      }
+    if (hi == 0) {
+      float *md = p.md_cap + (((size_t)blockIdx.x * kBQ + row) * T + j) * 2;
+      md[0] = st.m;
+      md[1] = st.dsum;
+    }
+  }
+
+  // ---- partial^T = V_j^T . P8^T (FP32, fresh), then RO = RO * alpha + partial ----
+  const v16f zero16 = {};
+  v16f part[NS];
+#pragma unroll
+  for (int cb = 0; cb < NS; ++cb) {
+    const v4i a0 = *(const v4i *)(vl + (cb * 2 + 0) * 1024 + lane * 16);
+    const v4i a1 = *(const v4i *)(vl + (cb * 2 + 1) * 1024 + lane * 16);
+    const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    part[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pop, zero16, 0, 0, 0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int cb = 0; cb < NS; ++cb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) st.ro[cb][v] = __builtin_fmaf(st.ro[cb][v], alpha, part[cb][v]);
+
+  // tile j+1 landed (this wave's copies) and every wave is done with `cur`
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+template <int D, bool CAP>
+__global__ __launch_bounds__(256, kFwdBlocksPerCU) void k_attn_fwd(FwdParams p) {
   constexpr int NS = D / 32;                 // INT8 k-steps per key row == PV row blocks
   constexpr int TILE = kBK * D;              // bytes of one K (or V) tile
-  constexpr int NLD = 2 * TILE / (256 * 16); // 16-byte loads per thread per K+V tile
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * TILE];
+  // two LDS buffers of [K tile | V tile], alternating per tile
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2 * TILE];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int u;
@@ -69,6 +231,11 @@ __global__ __launch_bounds__(256) void k_attn_fwd(FwdParams p) {
   }
   const int bh = u / p.nqb, qb = u - bh * p.nqb;
   const int T = p.T;
+  const int8_t *kg = p.k_codes + (size_t)bh * T * TILE;
+  const uint8_t *vg = p.v_codes + (size_t)bh * T * TILE;
+  const float *ksc = p.k_scale + (size_t)bh * T;
+
+  issue_tile<D>(lds_a, kg, vg, 0, wave, lane);
 
   // Q^T operand (B of the INT8 product) for this wave's 32 rows, kept in registers.
   v4i qop[NS];
@@ -77,166 +244,44 @@ __global__ __launch_bounds__(256) void k_attn_fwd(FwdParams p) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) qop[s] = *(const v4i *)(qsrc + s * 1024);
   }
-  const float sq = p.q_scale[u];
-  const int8_t *kg = p.k_codes + (size_t)bh * T * TILE;
-  const uint8_t *vg = p.v_codes + (size_t)bh * T * TILE;
-  const float *ksc = p.k_scale + (size_t)bh * T;
-
-  // chunk i of this thread: 16 bytes at offset (i*256 + tid)*16 of [K tile | V tile]
-  const uint8_t *gsrc[NLD];
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int idx = i * 256 + tid;
-    gsrc[i] = idx < TILE / 16 ? (const uint8_t *)kg + idx * 16 : vg + (idx - TILE / 16) * 16;
-  }
-  uint4 pre[NLD];
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) pre[i] = *(const uint4 *)gsrc[i];
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) *(uint4 *)(&lds[0][(i * 256 + tid) * 16]) = pre[i];
-  __syncthreads();
-
-  float m = -INFINITY, dsum = 0.f;
-  v16f ro[NS];
-#pragma unroll
-  for (int c = 0; c < NS; ++c)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) ro[c][v] = 0.f;
-  const v16f zero16 = {};
-  const int hi = lane >> 5;            // which 4-key group of each 8 this lane holds
+  const float sq = load_uniform(p.q_scale + u);
   const int row = wave * 32 + (lane & 31);
 
+  FwdState<D> st;
+  st.m = -INFINITY;
+  st.dsum = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < NS; ++cb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) st.ro[cb][v] = 0.f;
+
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+#pragma nounroll
   for (int j = 0; j < T; ++j) {
-    const int buf = j & 1;
-    // next tile's loads are always issued (the last iteration reloads its own
-    // tile into the idle buffer), which keeps the ring free of branches
-    const size_t jn = (size_t)min(j + 1, T - 1) * TILE;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) pre[i] = *(const uint4 *)(gsrc[i] + jn);
-    const uint8_t *kl = lds[buf];
-    const uint8_t *vl = lds[buf] + TILE;
-
-    // ---- S^T = K_j . Q^T (int32, exact) ----
-    v16i sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = (v16i){};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const v4i a = *(const v4i *)(kl + (kb * NS + s) * 1024 + lane * 16);
-        sacc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[s], sacc[kb], 0, 0, 0);
-      }
-    }
-    if (CAP) {
-      int32_t *sc = p.s_cap + ((size_t)blockIdx.x * kBQ + row) * ((size_t)T * kBK) + (size_t)j * kBK;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sc[kb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3)] = sacc[kb][v];
-    }
-    // ragged tail: keys >= Nkv of the last tile take no part in max, sum or PV
-    const int kvalid = p.Nkv - j * kBK;
-    const bool masked = kvalid < kBK;
-    if (masked) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (kb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3) >= kvalid) sacc[kb][v] = INT_MIN;
-    }
-
-    // ---- online softmax: max in the integer domain (the per-tile factor is >= 0) ----
-    int mx = sacc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = max(mx, sacc[kb][v]);
-    mx = partner_max(mx);
-    const float c = (sq * ksc[j]) * p.sl2;        // fp32(fp32(sq * sk_j) * sl2)
-    const float mnew = fmaxf(m, (float)mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);   // "rescale"; 0 on the first tile
-    const float nb = kLog2_448 - mnew;
-    float pv[2][16];
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        pv[kb][v] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sacc[kb][v], c, nb));
-      }
-    if (masked) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (kb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3) >= kvalid) pv[kb][v] = 0.f;
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) ls += pv[kb][v];
-    ls = partner_sum(ls);
-    dsum = __builtin_fmaf(dsum, alpha, ls);        // d carries the factor 448
-    m = mnew;
-
-    // ---- P8 (E4M3FN, RNE) packed straight into the B operand of the PV product ----
-    v8i pop;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int kb = w >> 2, v0 = 4 * (w & 3);
-      int x = __builtin_amdgcn_cvt_pk_fp8_f32(pv[kb][v0], pv[kb][v0 + 1], 0, false);
-      x = __builtin_amdgcn_cvt_pk_fp8_f32(pv[kb][v0 + 2], pv[kb][v0 + 3], x, true);
-      pop[w] = x;
-    }
-    if (CAP) {
-      uint8_t *pc = p.p8_cap + ((size_t)blockIdx.x * kBQ + row) * ((size_t)T * kBK) + (size_t)j * kBK;
-#pragma unroll
-      for (int w = 0; w < 8; ++w)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * (w & 3) + e;
-          pc[(w >> 2) * 32 + 8 * (v >> 2) + 4 * hi + (v & 3)] = (uint8_t)((uint32_t)pop[w] >> (8 * e));
-        }
-      if (hi == 0) {
-        float *md = p.md_cap + (((size_t)blockIdx.x * kBQ + row) * T + j) * 2;
-        md[0] = m;
-        md[1] = dsum;
-      }
-    }
-
-    // ---- partial^T = V_j^T . P8^T (FP32), then RO = RO * alpha + partial ----
-#pragma unroll
-    for (int c = 0; c < NS; ++c) {
-      const v4i a0 = *(const v4i *)(vl + (c * 2 + 0) * 1024 + lane * 16);
-      const v4i a1 = *(const v4i *)(vl + (c * 2 + 1) * 1024 + lane * 16);
-      const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      const v16f part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pop, zero16, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) ro[c][v] = __builtin_fmaf(ro[c][v], alpha, part[v]);
-    }
-
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) *(uint4 *)(&lds[buf ^ 1][(i * 256 + tid) * 16]) = pre[i];
-    __syncthreads();
+    uint8_t *cur = (j & 1) ? lds_b : lds_a;
+    uint8_t *nxt = (j & 1) ? lds_a : lds_b;
+    tile_step<D, CAP>(p, st, qop, sq, j, cur, nxt, kg, vg, ksc, wave, lane, row);
   }
 
   // ---- final conversion: reciprocal of d, per-channel V scale, BF16 ----
+  const int hi = lane >> 5;
   const int n = qb * kBQ + row;
   if (n < p.Nq) {
-    const float r = 1.0f / dsum;                  // "reciprocal" (d includes the 448)
+    const float r = 1.0f / st.dsum;               // "reciprocal" (d includes the 448)
     const int b = bh / p.H, h = bh - b * p.H;
     uint16_t *orow = p.out + b * p.os[0] + h * p.os[1] + (int64_t)n * p.os[2];
     const float *vs = p.v_scale + (size_t)bh * D;
 #pragma unroll
-    for (int c = 0; c < NS; ++c)
+    for (int cb = 0; cb < NS; ++cb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int ch = 32 * c + 8 * q4 + 4 * hi;
+        const int ch = 32 * cb + 8 * q4 + 4 * hi;
         uint32_t w[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const float o0 = (ro[c][4 * q4 + 2 * e] * r) * vs[ch + 2 * e];
-          const float o1 = (ro[c][4 * q4 + 2 * e + 1] * r) * vs[ch + 2 * e + 1];
+          const float o0 = (st.ro[cb][4 * q4 + 2 * e] * r) * vs[ch + 2 * e];
+          const float o1 = (st.ro[cb][4 * q4 + 2 * e + 1] * r) * vs[ch + 2 * e + 1];
           const __bf16 b0 = (__bf16)o0, b1 = (__bf16)o1;
           w[e] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
         }
