@@ -98,6 +98,9 @@ def main():
     ap.add_argument("--workload", default="long_video")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention to time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a kernel of known "
+                         "HBM traffic, used to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)"
@@ -179,6 +182,14 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calibration_copy_bytes"] = n
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
