@@ -1,0 +1,111 @@
+"""GPU-path invariants that hold exactly, plus graph capture and repetition.
+
+Exact by construction of the method (and so bit-exact on the GPU too):
+  * V * 2 -> O * 2 (the per-channel V scale absorbs the factor exactly);
+  * a joint permutation of the channels of Q, K, V permutes O's channels
+    (integer scores are exact; each output channel sees the same products);
+  * a permutation of query rows inside one 128-row block permutes O's rows.
+Determinism: repeated launches give identical bytes (the pages' prototype was
+checked over 1,000 launches, "Experiment Log", Phase 2B).
+Graph capture: prep + forward captured once and replayed gives the eager
+result every time (the library allocates nothing and never synchronizes).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from quantized_exact_attention_amd import sage
+from quantized_exact_attention_amd.synth import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _run(q, k, v, sm_scale=None):
+    return sage.sage_attention(q.to(DEV), k.to(DEV), v.to(DEV), sm_scale).cpu()
+
+
+def _bits(t):
+    return t.view(torch.int16)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_v_times_two_doubles_output_exactly(D):
+    q, k, v = make_inputs(WORKLOADS["ragged_tails"], seed=11, B=1, H=2, Nq=300, Nkv=500, D=D)
+    a = _run(q, k, v)
+    b = _run(q, k, v * 2)
+    assert torch.equal(_bits(b), _bits(a * 2))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_channel_permutation_equivariance(D):
+    q, k, v = make_inputs(WORKLOADS["ragged_tails"], seed=12, B=1, H=2, Nq=260, Nkv=333, D=D)
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(D))
+    a = _run(q, k, v)
+    b = _run(q[..., perm].contiguous(), k[..., perm].contiguous(), v[..., perm].contiguous())
+    assert torch.equal(_bits(b), _bits(a[..., perm].contiguous()))
+
+
+def test_row_permutation_inside_a_block():
+    q, k, v = make_inputs(WORKLOADS["dit_block"], seed=13, B=1, H=1, Nq=256, Nkv=700, D=128)
+    rp = torch.cat([torch.from_numpy(np.random.default_rng(4).permutation(128)),
+                    128 + torch.from_numpy(np.random.default_rng(5).permutation(128))])
+    a = _run(q, k, v)
+    b = _run(q[:, :, rp].contiguous(), k, v)
+    assert torch.equal(_bits(b), _bits(a[:, :, rp].contiguous()))
+
+
+def test_strided_output_view():
+    q, k, v = make_inputs(WORKLOADS["ragged_tails"], seed=14, B=2, H=3, Nq=150, Nkv=90, D=128)
+    quant = sage.sage_quant_prep(q.to(DEV), k.to(DEV), v.to(DEV))
+    dense = sage.sage_attn_fwd(quant)
+    store = torch.zeros(2, 150, 3, 128, dtype=torch.bfloat16, device=DEV)   # [B,N,H,D] memory
+    view = store.transpose(1, 2)
+    sage.sage_attn_fwd(quant, out=view)
+    assert torch.equal(_bits(view.contiguous()), _bits(dense.contiguous()))
+
+
+def test_thousand_launches_bit_identical():
+    q, k, v = make_inputs(WORKLOADS["ragged_tails"])
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    quant = sage.sage_quant_prep(qd, kd, vd)
+    first = sage.sage_attn_fwd(quant).clone()
+    out = torch.empty_like(first)
+    mismatches = torch.zeros((), dtype=torch.int64, device=DEV)
+    for i in range(1000):
+        if i % 10 == 0:
+            sage.sage_quant_prep(qd, kd, vd, out=quant)
+        sage.sage_attn_fwd(quant, out=out)
+        mismatches += (_bits(out) != _bits(first)).sum()
+    torch.cuda.synchronize()
+    assert int(mismatches) == 0
+
+
+def test_graph_capture_replay_matches_eager():
+    w = WORKLOADS["ragged_tails"]
+    q, k, v = make_inputs(w, seed=21, B=1, H=4, Nq=500, Nkv=700, D=128)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    quant = sage.sage_quant_prep(qd, kd, vd)
+    out = sage.sage_attn_fwd(quant)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            sage.sage_quant_prep(qd, kd, vd, out=quant)
+            sage.sage_attn_fwd(quant, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    for r in range(4):
+        # new inputs written in place, then replay, then compare with an eager run
+        q2, k2, v2 = make_inputs(w, seed=100 + r, B=1, H=4, Nq=500, Nkv=700, D=128)
+        qd.copy_(q2.to(DEV))
+        kd.copy_(k2.to(DEV))
+        vd.copy_(v2.to(DEV))
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = out.clone()
+        eager = sage.sage_attention(qd, kd, vd)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(replayed), _bits(eager)), "replay %d differs" % r
