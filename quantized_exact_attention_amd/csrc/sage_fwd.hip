@@ -49,10 +49,10 @@ __device__ __forceinline__ float partner_sum(float x) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Three 4-wave workgroups per CU (3 waves per SIMD): the register budget is
-// 168 VGPRs per lane, which the per-wave state (RO 64, S/p 32, P8 8, Q 16,
-// partial 16-64) fits.
-constexpr int kFwdBlocksPerCU = 3;
+// Waves per SIMD: 3 at D = 128 (168 VGPRs per lane, which the per-wave state
+// RO 64, S/p 32, P8 8, Q 16, partial 16-64 fits), 4 at D = 64 (128 VGPRs; the
+// few values that do not fit are spilled outside the tile loop only).
+template <int D> struct FwdOccupancy { static constexpr int waves_per_simd = D == 128 ? 3 : 4; };
 
 // log2(448): P is produced directly as 448 * 2^(s - m) = 2^(s - m + log2 448).
 constexpr float kLog2_448 = 8.80735492205760410744f;
@@ -214,7 +214,7 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
 }
 
 template <int D, bool CAP>
-__global__ __launch_bounds__(256, kFwdBlocksPerCU) void k_attn_fwd(FwdParams p) {
+__global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_fwd(FwdParams p) {
   constexpr int NS = D / 32;                 // INT8 k-steps per key row == PV row blocks
   constexpr int TILE = kBK * D;              // bytes of one K (or V) tile
   // two LDS buffers of [K tile | V tile], alternating per tile

@@ -59,12 +59,18 @@ __device__ __forceinline__ uint32_t pack_i8x4(const float *x, float inv) {
 // ---- 1. per (b,h, key chunk): FP64 column sums of K (exact for bf16 data) and
 //         column max |V|; partials go to the workspace --------------------------
 template <int D>
-__global__ __launch_bounds__(256) void k_prep_stats(PrepParams p) {
-  constexpr int CG = D / 8;      // 8-channel groups of one row
-  constexpr int TL = 256 / CG;   // rows handled in parallel
-  __shared__ double s_sum[TL][D];
-  __shared__ float s_max[TL][D];
-  const int chunk = blockIdx.x, bh = blockIdx.y;
+struct StatsSmem {
+  static constexpr int CG = D / 8;      // 8-channel groups of one row
+  static constexpr int TL = 256 / CG;   // rows handled in parallel
+  double sum[TL][D];
+  float max[TL][D];
+};
+
+template <int D>
+__device__ __forceinline__ void prep_stats_block(const PrepParams &p, int chunk, int bh, StatsSmem<D> &sm) {
+  constexpr int CG = StatsSmem<D>::CG, TL = StatsSmem<D>::TL;
+  auto &s_sum = sm.sum;
+  auto &s_max = sm.max;
   const int b = bh / p.H, h = bh - b * p.H;
   const int cg = threadIdx.x % CG, tl = threadIdx.x / CG;
   const int n0 = chunk * kStatChunk, n1 = min(p.Nkv, n0 + kStatChunk);
@@ -98,27 +104,37 @@ __global__ __launch_bounds__(256) void k_prep_stats(PrepParams p) {
 }
 
 // ---- 2. per (b,h): K mean, V channel scale and inverse -------------------------
+// 256 threads: channel c = t % D, chunk group t / D; the partial sums are exact,
+// so their order does not matter.
 template <int D>
-__global__ __launch_bounds__(D) void k_prep_finalize(PrepParams p) {
-  const int bh = blockIdx.x, c = threadIdx.x;
+__global__ __launch_bounds__(256) void k_prep_finalize(PrepParams p) {
+  constexpr int NG = 256 / D;
+  __shared__ double s_sum[NG][D];
+  __shared__ float s_max[NG][D];
+  const int bh = blockIdx.x, c = threadIdx.x % D, g = threadIdx.x / D;
   double s = 0.0;
   float mx = 0.f;
-  for (int i = 0; i < p.nchunk; ++i) {
+  for (int i = g; i < p.nchunk; i += NG) {
     const size_t o = ((size_t)bh * p.nchunk + i) * D + c;
     s += p.ws_ksum[o];
     mx = fmaxf(mx, p.ws_vmax[o]);
   }
-  p.k_mean[bh * D + c] = (float)(s / (double)p.Nkv);   // FP64 quotient, one FP32 rounding
-  p.v_scale[bh * D + c] = mx > 0.f ? mx / 448.0f : 0.f;  // correctly rounded FP32 divides
-  p.ws_vinv[bh * D + c] = mx > 0.f ? 448.0f / mx : 0.f;
+  s_sum[g][c] = s;
+  s_max[g][c] = mx;
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int i = 1; i < NG; ++i) { s += s_sum[i][c]; mx = fmaxf(mx, s_max[i][c]); }
+    p.k_mean[bh * D + c] = (float)(s / (double)p.Nkv);   // FP64 quotient, one FP32 rounding
+    p.v_scale[bh * D + c] = mx > 0.f ? mx / 448.0f : 0.f;  // correctly rounded FP32 divides
+    p.ws_vinv[bh * D + c] = mx > 0.f ? 448.0f / mx : 0.f;
+  }
 }
 
 // ---- 3. Q: per 128-row block INT8 --------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void k_quant_q(PrepParams p) {
+__device__ __forceinline__ void quant_q_block(const PrepParams &p, int qb, int bh, float *red) {
   constexpr int UPR = D / 16, UPT = kBQ * UPR / 256;
-  __shared__ float red[4];
-  const int qb = blockIdx.x, bh = blockIdx.y;
   const int b = bh / p.H, h = bh - b * p.H;
   const uint16_t *base = p.q + b * p.qs[0] + h * p.qs[1];
   float x[UPT][16];
@@ -155,10 +171,8 @@ __global__ __launch_bounds__(256) void k_quant_q(PrepParams p) {
 
 // ---- 4. K: smoothing, then per 64-row block INT8 -------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void k_quant_k(PrepParams p) {
+__device__ __forceinline__ void quant_k_block(const PrepParams &p, int j, int bh, float *red) {
   constexpr int UPR = D / 16, UPT = kBK * UPR / 256;
-  __shared__ float red[4];
-  const int j = blockIdx.x, bh = blockIdx.y;
   const int b = bh / p.H, h = bh - b * p.H;
   const uint16_t *base = p.k + b * p.ks[0] + h * p.ks[1];
   const float *mean = p.k_mean + (size_t)bh * D;
@@ -201,11 +215,15 @@ __global__ __launch_bounds__(256) void k_quant_k(PrepParams p) {
 // (channel block, half, lane) unit: byte e holds key 32*half + 8*(e/4) +
 // 4*(lane/32) + e%4 of channel 32*block + lane%32.
 template <int D>
-__global__ __launch_bounds__(256) void k_quant_v(PrepParams p) {
+struct VTileSmem {
+  uint16_t tile[kBK][D + 2];                 // +2 shifts rows across banks
+};
+
+template <int D>
+__device__ __forceinline__ void quant_v_block(const PrepParams &p, int j, int bh, VTileSmem<D> &sm) {
   constexpr int UPR = D / 8;                 // 8-value loads per row
   constexpr int NUNIT = (D / 32) * 2 * 64;   // 16-byte output units per tile
-  __shared__ uint16_t tile[kBK][D + 2];      // +2 shifts rows across banks
-  const int j = blockIdx.x, bh = blockIdx.y;
+  auto &tile = sm.tile;
   const int b = bh / p.H, h = bh - b * p.H;
   const uint16_t *base = p.v + b * p.vs[0] + h * p.vs[1];
   for (int u = threadIdx.x; u < kBK * UPR; u += 256) {
@@ -243,14 +261,31 @@ __global__ __launch_bounds__(256) void k_quant_v(PrepParams p) {
   }
 }
 
+// ---- launches: [stats | Q quant] -> finalize -> [K quant | V quant] ------------
+// Q quantization does not depend on the statistics, so it shares the first
+// launch; K and V quantization share the last one.
+template <int D>
+__global__ __launch_bounds__(256) void k_prep_pass1(PrepParams p) {
+  __shared__ StatsSmem<D> sm;
+  const int bh = blockIdx.y;
+  if ((int)blockIdx.x < p.nchunk) prep_stats_block<D>(p, blockIdx.x, bh, sm);
+  else quant_q_block<D>(p, blockIdx.x - p.nchunk, bh, (float *)&sm);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_prep_pass2(PrepParams p) {
+  __shared__ VTileSmem<D> sm;
+  const int bh = blockIdx.y;
+  if ((int)blockIdx.x < p.T) quant_k_block<D>(p, blockIdx.x, bh, (float *)&sm);
+  else quant_v_block<D>(p, blockIdx.x - p.T, bh, sm);
+}
+
 template <int D>
 static hipError_t launch_prep_d(const PrepParams &p, hipStream_t st) {
   const int BH = p.B * p.H;
-  hipLaunchKernelGGL(k_prep_stats<D>, dim3(p.nchunk, BH), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(k_prep_finalize<D>, dim3(BH), dim3(D), 0, st, p);
-  hipLaunchKernelGGL(k_quant_q<D>, dim3(p.nqb, BH), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(k_quant_k<D>, dim3(p.T, BH), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(k_quant_v<D>, dim3(p.T, BH), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(k_prep_pass1<D>, dim3(p.nchunk + p.nqb, BH), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(k_prep_finalize<D>, dim3(BH), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(k_prep_pass2<D>, dim3(2 * p.T, BH), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
