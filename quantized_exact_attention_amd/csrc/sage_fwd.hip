@@ -132,13 +132,17 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   }
 
   // ---- online softmax; max in the integer domain (the per-tile factor is >= 0) ----
-  int mx8[8];
+  // 32 values -> 16 three-input maxima in a tree of depth 3 (+1 two-input)
+  int m10[11];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int kb = i >> 2, v0 = 4 * (i & 3);
-    mx8[i] = max(max(sacc[kb][v0], sacc[kb][v0 + 1]), max(sacc[kb][v0 + 2], sacc[kb][v0 + 3]));
+  for (int i = 0; i < 10; ++i) {
+    const int x = 3 * i;
+    m10[i] = max(max(sacc[x >> 4][x & 15], sacc[(x + 1) >> 4][(x + 1) & 15]), sacc[(x + 2) >> 4][(x + 2) & 15]);
   }
-  int mx = max(max(max(mx8[0], mx8[1]), max(mx8[2], mx8[3])), max(max(mx8[4], mx8[5]), max(mx8[6], mx8[7])));
+  m10[10] = max(sacc[1][14], sacc[1][15]);
+  const int m4a = max(max(m10[0], m10[1]), m10[2]), m4b = max(max(m10[3], m10[4]), m10[5]);
+  const int m4c = max(max(m10[6], m10[7]), m10[8]), m4d = max(m10[9], m10[10]);
+  int mx = max(max(max(m4a, m4b), m4c), m4d);
   mx = partner_max(mx);
   const float c = (sq * load_uniform(ksc + j)) * p.sl2;   // fp32(fp32(sq * sk_j) * sl2)
   const float mnew = fmaxf(st.m, (float)mx * c);
@@ -173,7 +177,9 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     const int kb = w >> 2, v0 = 4 * (w & 3);
-    int x = __builtin_amdgcn_cvt_pk_fp8_f32(pv[kb][v0], pv[kb][v0 + 1], 0, false);
+    // the high half is written next, so the first conversion's "old" operand
+    // can be any dead register (no zeroing move)
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(pv[kb][v0], pv[kb][v0 + 1], __float_as_int(pv[kb][v0 + 1]), false);
     x = __builtin_amdgcn_cvt_pk_fp8_f32(pv[kb][v0 + 2], pv[kb][v0 + 3], x, true);
     pop[w] = x;
   }
@@ -221,7 +227,9 @@ __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_f
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2 * TILE];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2 * TILE];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar: tile-copy addresses and LDS bases stay in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int u;
   if (CAP) {
     u = p.units[blockIdx.x];
