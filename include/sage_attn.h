@@ -115,7 +115,7 @@ int sage_buffer_bytes(const sage_shape_t *shape, int which, size_t *bytes);
  *     code = RNE(fp32(x * fp32(127/A))) in [-127, 127]; A = 0 -> all zero
  *   V per channel: v_scale = fp32(vamax/448), code = E4M3FN_RNE(fp32(v * fp32(448/vamax)))
  * q, k, v: bf16 device tensors with strides->q/k/v.  Writes every buffer of
- * `quant` (including the workspace).  Launches 5 kernels on `stream`.
+ * `quant` (including the workspace).  Launches 3 kernels on `stream`.
  */
 int sage_quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *shape,
                     const sage_strides_t *strides, const sage_quant_t *quant, void *stream);

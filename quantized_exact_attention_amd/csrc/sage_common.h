@@ -16,7 +16,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // of 64 one-byte rows at D = 128, "Experiment Log", Phase 2A capability decision).
 constexpr int kBQ = 128;
 constexpr int kBK = 64;
-constexpr int kStatChunk = 512;   // keys per block of the K/V statistics pass
+constexpr int kStatChunk = 256;   // keys per block of the K/V statistics pass
 
 struct PrepParams {
   const uint16_t *q, *k, *v;      // bf16 bits

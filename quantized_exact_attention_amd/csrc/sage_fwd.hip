@@ -265,12 +265,23 @@ __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_f
 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  // The SIMD issues from its oldest ready wave first, so of the workgroups that
+  // share a CU the first one runs ahead and the grid ends with CUs holding one
+  // or two workgroups.  Stepping the wave priority down each quarter of the
+  // traversal lets the workgroups that are behind catch up.
+  const int q1 = T / 4, q2 = T / 2, q3 = (3 * T) / 4;
+  __builtin_amdgcn_s_setprio(3);
 #pragma nounroll
   for (int j = 0; j < T; ++j) {
+    if (j == q1) __builtin_amdgcn_s_setprio(2);
+    if (j == q2) __builtin_amdgcn_s_setprio(1);
+    if (j == q3) __builtin_amdgcn_s_setprio(0);
     uint8_t *cur = (j & 1) ? lds_b : lds_a;
     uint8_t *nxt = (j & 1) ? lds_a : lds_b;
     tile_step<D, CAP>(p, st, qop, sq, j, cur, nxt, kg, vg, ksc, wave, lane, row);
   }
+
+  __builtin_amdgcn_s_setprio(3);                 // finish and free the slot quickly
 
   // ---- final conversion: reciprocal of d, per-channel V scale, BF16 ----
   const int hi = lane >> 5;

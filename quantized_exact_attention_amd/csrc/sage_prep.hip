@@ -58,6 +58,9 @@ __device__ __forceinline__ uint32_t pack_i8x4(const float *x, float inv) {
 
 // ---- 1. per (b,h, key chunk): FP64 column sums of K (exact for bf16 data) and
 //         column max |V|; partials go to the workspace --------------------------
+// Thread (cg, tl) reads the 8-channel group cg of rows n0 + tl + TL*i; the loads
+// of kBatch rows are issued before any is used, so each thread keeps 2*kBatch
+// 16-byte loads in flight.
 template <int D>
 struct StatsSmem {
   static constexpr int CG = D / 8;      // 8-channel groups of one row
@@ -66,28 +69,45 @@ struct StatsSmem {
   float max[TL][D];
 };
 
+constexpr int kBatch = 8;
+
 template <int D>
 __device__ __forceinline__ void prep_stats_block(const PrepParams &p, int chunk, int bh, StatsSmem<D> &sm) {
-  constexpr int CG = StatsSmem<D>::CG, TL = StatsSmem<D>::TL;
+  constexpr int CG = StatsSmem<D>::CG, TL = StatsSmem<D>::TL, RPT = kStatChunk / TL;
+  static_assert(RPT % kBatch == 0, "rows per thread must be a multiple of the load batch");
   auto &s_sum = sm.sum;
   auto &s_max = sm.max;
   const int b = bh / p.H, h = bh - b * p.H;
   const int cg = threadIdx.x % CG, tl = threadIdx.x / CG;
-  const int n0 = chunk * kStatChunk, n1 = min(p.Nkv, n0 + kStatChunk);
+  const int n0 = chunk * kStatChunk + tl;
   const uint16_t *kb = p.k + b * p.ks[0] + h * p.ks[1] + cg * 8;
   const uint16_t *vb = p.v + b * p.vs[0] + h * p.vs[1] + cg * 8;
   double acc[8];
   float vmx[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) { acc[e] = 0.0; vmx[e] = 0.f; }
-  for (int n = n0 + tl; n < n1; n += TL) {
-    float kf[8], vf[8];
-    unpack8(*(const uint4 *)(kb + (int64_t)n * p.ks[2]), kf);
-    unpack8(*(const uint4 *)(vb + (int64_t)n * p.vs[2]), vf);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[e] += (double)kf[e];
-      vmx[e] = fmaxf(vmx[e], fabsf(vf[e]));
+  for (int i0 = 0; i0 < RPT; i0 += kBatch) {
+    uint4 kr[kBatch], vr[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int n = n0 + (i0 + i) * TL;
+      kr[i] = vr[i] = make_uint4(0, 0, 0, 0);    // rows past Nkv add 0 and max 0
+      if (n < p.Nkv) {
+        kr[i] = *(const uint4 *)(kb + (int64_t)n * p.ks[2]);
+        vr[i] = *(const uint4 *)(vb + (int64_t)n * p.vs[2]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      float kf[8], vf[8];
+      unpack8(kr[i], kf);
+      unpack8(vr[i], vf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc[e] += (double)kf[e];
+        vmx[e] = fmaxf(vmx[e], fabsf(vf[e]));
+      }
     }
   }
 #pragma unroll
@@ -103,147 +123,150 @@ __device__ __forceinline__ void prep_stats_block(const PrepParams &p, int chunk,
   }
 }
 
-// ---- 2. per (b,h): K mean, V channel scale and inverse -------------------------
-// 256 threads: channel c = t % D, chunk group t / D; the partial sums are exact,
-// so their order does not matter.
+// ---- 2. per (b,h, 16 channels): K mean, V channel scale and inverse ------------
+// 256 threads: channel 16*blockIdx.y + t % 16, chunk group t / 16; the partial
+// sums are exact, so their order does not matter.
 template <int D>
 __global__ __launch_bounds__(256) void k_prep_finalize(PrepParams p) {
-  constexpr int NG = 256 / D;
-  __shared__ double s_sum[NG][D];
-  __shared__ float s_max[NG][D];
-  const int bh = blockIdx.x, c = threadIdx.x % D, g = threadIdx.x / D;
+  constexpr int NG = 16, U = 4;
+  __shared__ double s_sum[NG][16];
+  __shared__ float s_max[NG][16];
+  const int bh = blockIdx.x, cl = threadIdx.x % 16, g = threadIdx.x / 16, c = blockIdx.y * 16 + cl;
   double s = 0.0;
   float mx = 0.f;
-  for (int i = g; i < p.nchunk; i += NG) {
-    const size_t o = ((size_t)bh * p.nchunk + i) * D + c;
-    s += p.ws_ksum[o];
-    mx = fmaxf(mx, p.ws_vmax[o]);
+  for (int i0 = g; i0 < p.nchunk; i0 += NG * U) {
+    double ps[U];
+    float pm[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * NG;
+      ps[u] = 0.0;
+      pm[u] = 0.f;
+      if (i < p.nchunk) {
+        const size_t o = ((size_t)bh * p.nchunk + i) * D + c;
+        ps[u] = p.ws_ksum[o];
+        pm[u] = p.ws_vmax[o];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) { s += ps[u]; mx = fmaxf(mx, pm[u]); }
   }
-  s_sum[g][c] = s;
-  s_max[g][c] = mx;
+  s_sum[g][cl] = s;
+  s_max[g][cl] = mx;
   __syncthreads();
   if (g == 0) {
 #pragma unroll
-    for (int i = 1; i < NG; ++i) { s += s_sum[i][c]; mx = fmaxf(mx, s_max[i][c]); }
+    for (int i = 1; i < NG; ++i) { s += s_sum[i][cl]; mx = fmaxf(mx, s_max[i][cl]); }
     p.k_mean[bh * D + c] = (float)(s / (double)p.Nkv);   // FP64 quotient, one FP32 rounding
     p.v_scale[bh * D + c] = mx > 0.f ? mx / 448.0f : 0.f;  // correctly rounded FP32 divides
     p.ws_vinv[bh * D + c] = mx > 0.f ? 448.0f / mx : 0.f;
   }
 }
 
-// ---- 3. Q: per 128-row block INT8 --------------------------------------------
+// ---- 3. INT8 block quantization of R rows (Q: 128, smoothed K: 64) ------------
+// Thread t owns the 8-channel units t + 256 i: row (t + 256 i) / (D/8), channels
+// 8 * (t % (D/8)) (the same for every i, since 256 is a multiple of D/8), so a
+// wave reads whole rows.  The raw bf16 words stay in registers and are unpacked
+// again for the codes; each unit becomes 8 bytes of a 16-byte operand unit.
+template <int D, int R, bool SMOOTH>
+__device__ __forceinline__ void quant_i8_rows(const uint16_t *base, int64_t rs, int nvalid, const float *mean,
+                                              int8_t *dst, float *scale_out, float *red) {
+  constexpr int UPR = D / 8, UPT = R * UPR / 256;
+  static_assert(256 % UPR == 0 && UPT >= 1, "unit mapping");
+  const int c8 = threadIdx.x % UPR, r0 = threadIdx.x / UPR;
+  uint4 raw[UPT];
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int r = r0 + i * (256 / UPR);
+    raw[i] = make_uint4(0, 0, 0, 0);             // pad rows are 0 and do not raise the max
+    if (r < nvalid) raw[i] = *(const uint4 *)(base + (int64_t)r * rs + c8 * 8);
+  }
+  float mu[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mu[e] = SMOOTH ? mean[c8 * 8 + e] : 0.f;
+  auto values = [&](int i, float *f) {
+    unpack8(raw[i], f);
+    if (SMOOTH && r0 + i * (256 / UPR) < nvalid) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = f[e] - mu[e];   // one FP32 rounding
+    }
+  };
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    float f[8];
+    values(i, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+  }
+  amax = block_max_nonneg(amax, red);
+  const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+  if (threadIdx.x == 0) *scale_out = amax > 0.f ? amax / 127.0f : 0.f;
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    float f[8];
+    values(i, f);
+    const int r = r0 + i * (256 / UPR);
+    uint2 w;
+    w.x = pack_i8x4(f, inv);
+    w.y = pack_i8x4(f + 4, inv);
+    *(uint2 *)(dst + i8_operand_offset<D>(r, c8 >> 1) + (c8 & 1) * 8) = w;
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void quant_q_block(const PrepParams &p, int qb, int bh, float *red) {
-  constexpr int UPR = D / 16, UPT = kBQ * UPR / 256;
   const int b = bh / p.H, h = bh - b * p.H;
-  const uint16_t *base = p.q + b * p.qs[0] + h * p.qs[1];
-  float x[UPT][16];
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < UPT; ++i) {
-    const int u = i * 256 + threadIdx.x, r = u / UPR, c16 = u % UPR, n = qb * kBQ + r;
-    if (n < p.Nq) {
-      const uint4 *src = (const uint4 *)(base + (int64_t)n * p.qs[2] + c16 * 16);
-      unpack8(src[0], x[i]);
-      unpack8(src[1], x[i] + 8);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) x[i][e] = 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
-  }
-  amax = block_max_nonneg(amax, red);
-  const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-  if (threadIdx.x == 0) p.q_scale[bh * p.nqb + qb] = amax > 0.f ? amax / 127.0f : 0.f;
-  int8_t *dst = p.q_codes + ((size_t)bh * p.nqb + qb) * kBQ * D;
-#pragma unroll
-  for (int i = 0; i < UPT; ++i) {
-    const int u = i * 256 + threadIdx.x, r = u / UPR, c16 = u % UPR;
-    uint4 w;
-    w.x = pack_i8x4(x[i] + 0, inv);
-    w.y = pack_i8x4(x[i] + 4, inv);
-    w.z = pack_i8x4(x[i] + 8, inv);
-    w.w = pack_i8x4(x[i] + 12, inv);
-    *(uint4 *)(dst + i8_operand_offset<D>(r, c16)) = w;
-  }
+  const uint16_t *base = p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)qb * kBQ * p.qs[2];
+  quant_i8_rows<D, kBQ, false>(base, p.qs[2], min(kBQ, p.Nq - qb * kBQ), nullptr,
+                               p.q_codes + ((size_t)bh * p.nqb + qb) * kBQ * D, p.q_scale + bh * p.nqb + qb, red);
 }
 
-// ---- 4. K: smoothing, then per 64-row block INT8 -------------------------------
-template <int D>
-__device__ __forceinline__ void quant_k_block(const PrepParams &p, int j, int bh, float *red) {
-  constexpr int UPR = D / 16, UPT = kBK * UPR / 256;
-  const int b = bh / p.H, h = bh - b * p.H;
-  const uint16_t *base = p.k + b * p.ks[0] + h * p.ks[1];
-  const float *mean = p.k_mean + (size_t)bh * D;
-  float x[UPT][16];
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < UPT; ++i) {
-    const int u = i * 256 + threadIdx.x, r = u / UPR, c16 = u % UPR, n = j * kBK + r;
-    if (n < p.Nkv) {
-      const uint4 *src = (const uint4 *)(base + (int64_t)n * p.ks[2] + c16 * 16);
-      unpack8(src[0], x[i]);
-      unpack8(src[1], x[i] + 8);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) x[i][e] = x[i][e] - mean[c16 * 16 + e];   // one FP32 rounding
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) x[i][e] = 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
-  }
-  amax = block_max_nonneg(amax, red);
-  const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-  if (threadIdx.x == 0) p.k_scale[(size_t)bh * p.T + j] = amax > 0.f ? amax / 127.0f : 0.f;
-  int8_t *dst = p.k_codes + ((size_t)bh * p.T + j) * kBK * D;
-#pragma unroll
-  for (int i = 0; i < UPT; ++i) {
-    const int u = i * 256 + threadIdx.x, r = u / UPR, c16 = u % UPR;
-    uint4 w;
-    w.x = pack_i8x4(x[i] + 0, inv);
-    w.y = pack_i8x4(x[i] + 4, inv);
-    w.z = pack_i8x4(x[i] + 8, inv);
-    w.w = pack_i8x4(x[i] + 12, inv);
-    *(uint4 *)(dst + i8_operand_offset<D>(r, c16)) = w;
-  }
-}
-
-// ---- 5. V: per-channel E4M3FN, written as the A operand of the PV product ------
-// A 64-key tile is staged in LDS, then each thread gathers the 16 bytes of one
+// ---- 4. one 64-key tile: K smoothing + per-tile INT8, and per-channel E4M3FN V -
+// written as the A operands of the two products.  Both tiles' loads are issued
+// first.  V is staged in LDS, then each thread gathers the 16 bytes of one
 // (channel block, half, lane) unit: byte e holds key 32*half + 8*(e/4) +
 // 4*(lane/32) + e%4 of channel 32*block + lane%32.
 template <int D>
-struct VTileSmem {
-  uint16_t tile[kBK][D + 2];                 // +2 shifts rows across banks
+struct KVTileSmem {
+  uint16_t tile[kBK][D + 8];                 // 16-byte aligned rows, +8 shifts rows across banks
+  float red[4];
 };
 
 template <int D>
-__device__ __forceinline__ void quant_v_block(const PrepParams &p, int j, int bh, VTileSmem<D> &sm) {
-  constexpr int UPR = D / 8;                 // 8-value loads per row
-  constexpr int NUNIT = (D / 32) * 2 * 64;   // 16-byte output units per tile
-  auto &tile = sm.tile;
+__device__ __forceinline__ void quant_kv_tile(const PrepParams &p, int j, int bh, KVTileSmem<D> &sm) {
+  constexpr int VU = D / 8, VUPT = kBK * VU / 256;    // V: 8-channel loads per thread
+  constexpr int NUNIT = (D / 32) * 2 * 64;            // 16-byte V output units per tile
   const int b = bh / p.H, h = bh - b * p.H;
-  const uint16_t *base = p.v + b * p.vs[0] + h * p.vs[1];
-  for (int u = threadIdx.x; u < kBK * UPR; u += 256) {
-    const int r = u / UPR, c8 = u % UPR, n = j * kBK + r;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (n < p.Nkv) w = *(const uint4 *)(base + (int64_t)n * p.vs[2] + c8 * 8);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  const int nvalid = min(kBK, p.Nkv - j * kBK);
+  const uint16_t *vbase = p.v + b * p.vs[0] + h * p.vs[1] + (int64_t)j * kBK * p.vs[2];
+  uint4 vraw[VUPT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[r][c8 * 8 + 2 * e] = (uint16_t)(ww[e] & 0xffffu);
-      tile[r][c8 * 8 + 2 * e + 1] = (uint16_t)(ww[e] >> 16);
-    }
+  for (int i = 0; i < VUPT; ++i) {
+    const int u = i * 256 + threadIdx.x, r = u / VU, c8 = u % VU;
+    vraw[i] = make_uint4(0, 0, 0, 0);
+    if (r < nvalid) vraw[i] = *(const uint4 *)(vbase + (int64_t)r * p.vs[2] + c8 * 8);
   }
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < VUPT; ++i) {
+    const int u = i * 256 + threadIdx.x, r = u / VU, c8 = u % VU;
+    *(uint4 *)&sm.tile[r][c8 * 8] = vraw[i];
+  }
+
+  // K: ks = fp32(K - mean), then the tile's INT8 scale and codes; the barriers of
+  // its block maximum also publish the V tile in LDS.
+  quant_i8_rows<D, kBK, true>(p.k + b * p.ks[0] + h * p.ks[1] + (int64_t)j * kBK * p.ks[2], p.ks[2], nvalid,
+                              p.k_mean + (size_t)bh * D, p.k_codes + ((size_t)bh * p.T + j) * kBK * D,
+                              p.k_scale + (size_t)bh * p.T + j, sm.red);
+
+  // V: code = E4M3FN_RNE(fp32(v * vinv_c)).
   const float *vinv = p.ws_vinv + (size_t)bh * D;
-  uint8_t *dst = p.v_codes + ((size_t)bh * p.T + j) * kBK * D;
+  uint8_t *vdst = p.v_codes + ((size_t)bh * p.T + j) * kBK * D;
+#pragma unroll
   for (int u = threadIdx.x; u < NUNIT; u += 256) {
     const int blk = u >> 7, half = (u >> 6) & 1, lane = u & 63;
     const int ch = 32 * blk + (lane & 31);
-    const float inv = vinv[ch];
+    const float vi = vinv[ch];
     uint32_t w[4];
 #pragma unroll
     for (int d4 = 0; d4 < 4; ++d4) {
@@ -251,19 +274,19 @@ __device__ __forceinline__ void quant_v_block(const PrepParams &p, int j, int bh
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = 32 * half + 8 * d4 + 4 * (lane >> 5) + e;
-        f[e] = bf16f(tile[key][ch]) * inv;
+        f[e] = bf16f(sm.tile[key][ch]) * vi;
       }
-      int x = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-      x = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], x, true);
-      w[d4] = (uint32_t)x;
+      int xw = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      xw = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], xw, true);
+      w[d4] = (uint32_t)xw;
     }
-    *(uint4 *)(dst + (size_t)u * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    *(uint4 *)(vdst + (size_t)u * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
-// ---- launches: [stats | Q quant] -> finalize -> [K quant | V quant] ------------
+// ---- launches: [stats | Q quant] -> finalize -> [K and V quant per tile] --------
 // Q quantization does not depend on the statistics, so it shares the first
-// launch; K and V quantization share the last one.
+// launch; one workgroup of the last launch quantizes the K and V rows of a tile.
 template <int D>
 __global__ __launch_bounds__(256) void k_prep_pass1(PrepParams p) {
   __shared__ StatsSmem<D> sm;
@@ -274,18 +297,16 @@ __global__ __launch_bounds__(256) void k_prep_pass1(PrepParams p) {
 
 template <int D>
 __global__ __launch_bounds__(256) void k_prep_pass2(PrepParams p) {
-  __shared__ VTileSmem<D> sm;
-  const int bh = blockIdx.y;
-  if ((int)blockIdx.x < p.T) quant_k_block<D>(p, blockIdx.x, bh, (float *)&sm);
-  else quant_v_block<D>(p, blockIdx.x - p.T, bh, sm);
+  __shared__ KVTileSmem<D> sm;
+  quant_kv_tile<D>(p, blockIdx.x, blockIdx.y, sm);
 }
 
 template <int D>
 static hipError_t launch_prep_d(const PrepParams &p, hipStream_t st) {
   const int BH = p.B * p.H;
   hipLaunchKernelGGL(k_prep_pass1<D>, dim3(p.nchunk + p.nqb, BH), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(k_prep_finalize<D>, dim3(BH), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(k_prep_pass2<D>, dim3(2 * p.T, BH), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(k_prep_finalize<D>, dim3(BH, D / 16), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(k_prep_pass2<D>, dim3(p.T, BH), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
