@@ -121,6 +121,24 @@ int sage_quant_prep(const void *q, const void *k, const void *v, const sage_shap
                     const sage_strides_t *strides, const sage_quant_t *quant, void *stream);
 
 /*
+ * The same stages in one pass over K and V (the fused preparation entry of
+ * "Experiment Log", Closed Prior Work: P1 entry fusion and P2 direct V
+ * preparation, and the matching rows of "Experiment Registry", Complete
+ * Registry): every workgroup keeps its K/V rows in registers while the
+ * workgroups of a head combine their column statistics, so K and V are read
+ * from memory once.  Arguments, layouts, results (bit-identical to
+ * sage_quant_prep), ownership and errors as for sage_quant_prep.  Used while a
+ * (b,h) needs at most 256 such workgroups (Nkv <= 65536 at D = 128, <= 131072 at
+ * D = 64); longer keys take sage_quant_prep's three launches.  Launches 2
+ * kernels on `stream`.  Its workgroups wait for each other inside the launch;
+ * the wait is bounded, and a wait that ran out leaves a nonzero status word in
+ * the workspace (never observed: the workgroups of a head are resident
+ * together).  Slower than sage_quant_prep on the shapes measured so far.
+ */
+int sage_quant_prep_single_pass(const void *q, const void *k, const void *v, const sage_shape_t *shape,
+                                const sage_strides_t *strides, const sage_quant_t *quant, void *stream);
+
+/*
  * Stages 3-5 ("Experiment Log", Phase 0 stage list and Phase 1 invariants;
  * checkpoint names of Phase 2B Fixed Aligned Numerical Prototype):
  * for each query row, 64-key tiles j = 0..T-1 strictly in order:

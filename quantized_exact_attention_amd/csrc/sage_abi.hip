@@ -61,7 +61,7 @@ size_t buffer_bytes(const sage_shape_t *s, int which) {
     case SAGE_BUF_K_MEAN: return BH * s->D * sizeof(float);
     case SAGE_BUF_WORKSPACE:
       return align256(ws_ksum_bytes((int)BH, nchunk, s->D)) + align256(ws_vmax_bytes((int)BH, nchunk, s->D)) +
-             align256(ws_vinv_bytes((int)BH, s->D));
+             align256(ws_vinv_bytes((int)BH, s->D)) + align256(ws_sync_bytes((int)BH));
     default: return 0;
   }
 }
@@ -165,8 +165,12 @@ int sage_buffer_bytes(const sage_shape_t *shape, int which, size_t *bytes) {
   return SAGE_OK;
 }
 
-int sage_quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *s,
-                    const sage_strides_t *st, const sage_quant_t *quant, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *s, const sage_strides_t *st,
+               const sage_quant_t *quant, void *stream, bool single_pass) {
   int r = check_shape(s);
   if (r) return r;
   if (!q || !k || !v || !st) return SAGE_E_NULL;
@@ -212,7 +216,26 @@ int sage_quant_prep(const void *q, const void *k, const void *v, const sage_shap
   p.ws_vmax = (float *)ws;
   ws += align256(ws_vmax_bytes(BH, p.nchunk, s->D));
   p.ws_vinv = (float *)ws;
+  ws += align256(ws_vinv_bytes(BH, s->D));
+  p.ws_sync = (uint32_t *)ws;
+  const int groups = ceil_div(s->Nkv, kFusedRows(s->D));
+  // G = 0: statistics, finalize and quantization launches
+  p.G = single_pass && groups <= kFusedMaxGroups ? groups : 0;
   return launch_prep(p, (hipStream_t)stream) == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sage_quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *s,
+                    const sage_strides_t *st, const sage_quant_t *quant, void *stream) {
+  return quant_prep(q, k, v, s, st, quant, stream, false);
+}
+
+int sage_quant_prep_single_pass(const void *q, const void *k, const void *v, const sage_shape_t *s,
+                                const sage_strides_t *st, const sage_quant_t *quant, void *stream) {
+  return quant_prep(q, k, v, s, st, quant, stream, true);
 }
 
 int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *s, float sm_scale, void *out,

@@ -33,6 +33,8 @@ struct PrepParams {
   double *ws_ksum;                // [B*H][nchunk][D]
   float *ws_vmax;                 // [B*H][nchunk][D]
   float *ws_vinv;                 // [B*H][D]
+  uint32_t *ws_sync;              // single-pass path: [B*H] arrivals, [B*H] ready flags, 1 status word
+  int G;                          // single-pass path: K/V workgroups per (b,h); 0 selects three launches
 };
 
 struct FwdParams {
@@ -58,6 +60,12 @@ struct FwdParams {
 inline size_t ws_ksum_bytes(int BH, int nchunk, int D) { return (size_t)BH * nchunk * D * sizeof(double); }
 inline size_t ws_vmax_bytes(int BH, int nchunk, int D) { return (size_t)BH * nchunk * D * sizeof(float); }
 inline size_t ws_vinv_bytes(int BH, int D) { return (size_t)BH * D * sizeof(float); }
+inline size_t ws_sync_bytes(int BH) { return ((size_t)2 * BH + 1) * sizeof(uint32_t); }
+
+// Single-pass prep: one workgroup holds kFusedRows(D) K and V rows in registers
+// (16 per thread); used while a head needs at most kFusedMaxGroups workgroups.
+constexpr int kFusedRows(int D) { return 16 * (256 / (D / 8)); }
+constexpr int kFusedMaxGroups = 256;
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 hipError_t launch_prep(const PrepParams &p, hipStream_t stream);

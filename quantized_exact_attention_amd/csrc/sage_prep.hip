@@ -284,6 +284,263 @@ __device__ __forceinline__ void quant_kv_tile(const PrepParams &p, int j, int bh
   }
 }
 
+// ---- single pass: K and V read from HBM once ----------------------------------
+// Workgroup (b,h, g) keeps rows [g*R, g*R + R) of K and V in registers, writes
+// their column partials and counts itself in; the last workgroup of the head
+// reduces the partials (K mean, V scale and inverse) and raises the head's
+// flag; every workgroup of the head waits for the flag, then quantizes its
+// rows.  The Q blocks take the grid's last workgroups.  Workgroups are
+// dispatched in index order and a head needs at most kFusedMaxGroups of them,
+// far fewer than fit on the device at once, so the workgroups of a head are
+// all resident before any waits for long; the wait is still bounded, and on
+// expiry the status word records it and the workgroup goes on.
+constexpr unsigned kSpinLimit = 1u << 19;   // x ~0.25 us of s_sleep: ~0.1 s
+
+// Data shared between the workgroups of a head (partials, K mean, V inverse)
+// is written and read with agent-scope atomic accesses, which go to the
+// device-coherent level instead of an XCD's own L2, so no L2 write-back or
+// invalidation is needed.  A store is ordered before the arrival count or the
+// ready flag by waiting until every store of the workgroup has completed.
+template <typename T>
+__device__ __forceinline__ void coherent_store(T *ptr, T v) {
+  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T coherent_load(const T *ptr) {
+  return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void completed_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores have completed
+  __syncthreads();
+}
+
+template <int D>
+struct FusedSmem {
+  static constexpr int CG = D / 8, TL = 256 / CG;
+  union {
+    struct {
+      double sum[TL][D];
+      float max[TL][D];
+    } st;
+    uint16_t tile[kBK][D + 8];
+  } u;
+  float red[kFusedRows(D) / kBK][4];
+  double fsum[256 / D][D];
+  float fmax[256 / D][D];
+  int last;
+};
+
+template <int D>
+__device__ __forceinline__ void fused_kv_group(const PrepParams &p, int bh, int g, FusedSmem<D> &sm) {
+  constexpr int CG = D / 8, TL = 256 / CG, RPT = 16, R = TL * RPT, TPW = R / kBK, RPTT = kBK / TL;
+  constexpr int NUNIT = (D / 32) * 2 * 64;
+  const int tid = threadIdx.x;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int cg = tid % CG, tl = tid / CG;
+  const int n0 = g * R + tl;
+  const uint16_t *kb = p.k + b * p.ks[0] + h * p.ks[1] + cg * 8;
+  const uint16_t *vb = p.v + b * p.vs[0] + h * p.vs[1] + cg * 8;
+  uint4 kr[RPT], vr[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int n = n0 + i * TL;
+    kr[i] = vr[i] = make_uint4(0, 0, 0, 0);    // rows past Nkv add 0 and max 0
+    if (n < p.Nkv) {
+      kr[i] = *(const uint4 *)(kb + (int64_t)n * p.ks[2]);
+      vr[i] = *(const uint4 *)(vb + (int64_t)n * p.vs[2]);
+    }
+  }
+
+  // ---- column partials of this group ----
+  {
+    double acc[8];
+    float vmx[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { acc[e] = 0.0; vmx[e] = 0.f; }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      float kf[8], vf[8];
+      unpack8(kr[i], kf);
+      unpack8(vr[i], vf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc[e] += (double)kf[e];
+        vmx[e] = fmaxf(vmx[e], fabsf(vf[e]));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { sm.u.st.sum[tl][cg * 8 + e] = acc[e]; sm.u.st.max[tl][cg * 8 + e] = vmx[e]; }
+  }
+  __syncthreads();
+  for (int c = tid; c < D; c += 256) {
+    double s = 0.0;
+    float mx = 0.f;
+    for (int i = 0; i < TL; ++i) { s += sm.u.st.sum[i][c]; mx = fmaxf(mx, sm.u.st.max[i][c]); }
+    const size_t o = ((size_t)bh * p.nchunk + g) * D + c;
+    coherent_store(p.ws_ksum + o, s);
+    coherent_store(p.ws_vmax + o, mx);
+  }
+  completed_barrier();                           // every partial of the group has reached memory
+  uint32_t *arrived = p.ws_sync + bh, *ready = p.ws_sync + p.B * p.H + bh, *status = p.ws_sync + 2 * p.B * p.H;
+  if (tid == 0)
+    sm.last = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(p.G - 1);
+  __syncthreads();
+
+  // ---- the last group of the head: K mean, V scale and inverse ----
+  if (sm.last) {
+    constexpr int NG = 256 / D;
+    const int c = tid % D, gi = tid / D;
+    double s = 0.0;
+    float mx = 0.f;
+    constexpr int U = 8;
+    for (int i0 = gi; i0 < p.G; i0 += NG * U) {
+      double ps[U];
+      float pm[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NG;
+        ps[u] = 0.0;
+        pm[u] = 0.f;
+        if (i < p.G) {
+          const size_t o = ((size_t)bh * p.nchunk + i) * D + c;
+          ps[u] = coherent_load(p.ws_ksum + o);
+          pm[u] = coherent_load(p.ws_vmax + o);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) { s += ps[u]; mx = fmaxf(mx, pm[u]); }   // exact sums: any order
+    }
+    sm.fsum[gi][c] = s;
+    sm.fmax[gi][c] = mx;
+    __syncthreads();
+    if (gi == 0) {
+#pragma unroll
+      for (int i = 1; i < NG; ++i) { s += sm.fsum[i][c]; mx = fmaxf(mx, sm.fmax[i][c]); }
+      coherent_store(p.k_mean + bh * D + c, (float)(s / (double)p.Nkv));   // FP64 quotient, one rounding
+      p.v_scale[bh * D + c] = mx > 0.f ? mx / 448.0f : 0.f;
+      coherent_store(p.ws_vinv + bh * D + c, mx > 0.f ? 448.0f / mx : 0.f);
+    }
+    completed_barrier();
+    if (tid == 0) __hip_atomic_store(ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid == 0) {
+    unsigned it = 0;
+    while (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      if (++it > kSpinLimit) {
+        __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  __syncthreads();
+
+  // ---- K: smoothing and per-tile INT8 ----
+  float mu[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mu[e] = coherent_load(p.k_mean + bh * D + cg * 8 + e);
+  auto kvals = [&](int i, float *f) {
+    unpack8(kr[i], f);
+    if (n0 + i * TL < p.Nkv) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = f[e] - mu[e];   // one FP32 rounding
+    }
+  };
+  {
+    uint32_t am[TPW];
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = q * RPTT; i < (q + 1) * RPTT; ++i) {
+        float f[8];
+        kvals(i, f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e]));
+      }
+      am[q] = __float_as_uint(a);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) am[q] = max(am[q], (uint32_t)__shfl_xor((int)am[q], o, 64));
+    }
+    if ((tid & 63) == 0) {
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) sm.red[q][tid >> 6] = __uint_as_float(am[q]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int j = g * TPW + q;                   // tile index in the head
+    if (j >= p.T) break;
+    const float amax = fmaxf(fmaxf(sm.red[q][0], sm.red[q][1]), fmaxf(sm.red[q][2], sm.red[q][3]));
+    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+    if (tid == 0) p.k_scale[(size_t)bh * p.T + j] = amax > 0.f ? amax / 127.0f : 0.f;
+    int8_t *kdst = p.k_codes + ((size_t)bh * p.T + j) * kBK * D;
+#pragma unroll
+    for (int i = q * RPTT; i < (q + 1) * RPTT; ++i) {
+      float f[8];
+      kvals(i, f);
+      const int r = tl + (i - q * RPTT) * TL;
+      uint2 w;
+      w.x = pack_i8x4(f, inv);
+      w.y = pack_i8x4(f + 4, inv);
+      *(uint2 *)(kdst + i8_operand_offset<D>(r, cg >> 1) + (cg & 1) * 8) = w;
+    }
+  }
+
+  // ---- V: per-channel E4M3FN, one tile at a time through LDS ----
+  const float *vinv = p.ws_vinv + (size_t)bh * D;
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int j = g * TPW + q;
+    if (j >= p.T) break;
+#pragma unroll
+    for (int i = q * RPTT; i < (q + 1) * RPTT; ++i) *(uint4 *)&sm.u.tile[tl + (i - q * RPTT) * TL][cg * 8] = vr[i];
+    __syncthreads();
+    uint8_t *vdst = p.v_codes + ((size_t)bh * p.T + j) * kBK * D;
+#pragma unroll
+    for (int uu = tid; uu < NUNIT; uu += 256) {
+      const int blk = uu >> 7, half = (uu >> 6) & 1, lane = uu & 63;
+      const int ch = 32 * blk + (lane & 31);
+      const float vi = coherent_load(vinv + ch);
+      uint32_t w[4];
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4) {
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 32 * half + 8 * d4 + 4 * (lane >> 5) + e;
+          f[e] = bf16f(sm.u.tile[key][ch]) * vi;
+        }
+        int xw = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+        xw = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], xw, true);
+        w[d4] = (uint32_t)xw;
+      }
+      *(uint4 *)(vdst + (size_t)uu * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    __syncthreads();
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_prep_fused(PrepParams p) {
+  __shared__ FusedSmem<D> sm;
+  const int nkv = p.B * p.H * p.G;
+  if ((int)blockIdx.x < nkv) {
+    const int bh = blockIdx.x / p.G;
+    fused_kv_group<D>(p, bh, blockIdx.x - bh * p.G, sm);
+  } else {
+    const int qi = blockIdx.x - nkv, bh = qi / p.nqb;
+    quant_q_block<D>(p, qi - bh * p.nqb, bh, &sm.red[0][0]);
+  }
+}
+
+// Zero the arrival counters, ready flags and status word of the single pass.
+__global__ __launch_bounds__(256) void k_prep_clear(uint32_t *w, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) w[i] = 0u;
+}
+
 // ---- launches: [stats | Q quant] -> finalize -> [K and V quant per tile] --------
 // Q quantization does not depend on the statistics, so it shares the first
 // launch; one workgroup of the last launch quantizes the K and V rows of a tile.
@@ -304,6 +561,12 @@ __global__ __launch_bounds__(256) void k_prep_pass2(PrepParams p) {
 template <int D>
 static hipError_t launch_prep_d(const PrepParams &p, hipStream_t st) {
   const int BH = p.B * p.H;
+  if (p.G > 0) {
+    const int nsync = 2 * BH + 1;
+    hipLaunchKernelGGL(k_prep_clear, dim3((nsync + 255) / 256), dim3(256), 0, st, p.ws_sync, nsync);
+    hipLaunchKernelGGL(k_prep_fused<D>, dim3(BH * p.G + BH * p.nqb), dim3(256), 0, st, p);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_prep_pass1<D>, dim3(p.nchunk + p.nqb, BH), dim3(256), 0, st, p);
   hipLaunchKernelGGL(k_prep_finalize<D>, dim3(BH, D / 16), dim3(256), 0, st, p);
   hipLaunchKernelGGL(k_prep_pass2<D>, dim3(p.T, BH), dim3(256), 0, st, p);

@@ -62,8 +62,9 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
         L.sage_buffer_bytes.argtypes = [ctypes.POINTER(SageShape), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
-        L.sage_quant_prep.argtypes = [vp, vp, vp, ctypes.POINTER(SageShape), ctypes.POINTER(SageStrides),
-                                      ctypes.POINTER(SageQuantC), vp]
+        for name in ("sage_quant_prep", "sage_quant_prep_single_pass"):
+            getattr(L, name).argtypes = [vp, vp, vp, ctypes.POINTER(SageShape), ctypes.POINTER(SageStrides),
+                                         ctypes.POINTER(SageQuantC), vp]
         L.sage_attn_fwd.argtypes = [ctypes.POINTER(SageQuantC), ctypes.POINTER(SageShape), f32, vp,
                                     ctypes.POINTER(SageStrides), vp]
         L.sage_attn_fwd_capture.argtypes = [ctypes.POINTER(SageQuantC), ctypes.POINTER(SageShape), f32, vp,
@@ -71,8 +72,8 @@ def lib() -> ctypes.CDLL:
         L.sage_device_check.argtypes = [ctypes.c_int]
         L.sage_status_string.argtypes = [ctypes.c_int]
         L.sage_status_string.restype = ctypes.c_char_p
-        for name in ("sage_buffer_bytes", "sage_quant_prep", "sage_attn_fwd", "sage_attn_fwd_capture",
-                     "sage_device_check"):
+        for name in ("sage_buffer_bytes", "sage_quant_prep", "sage_quant_prep_single_pass", "sage_attn_fwd",
+                     "sage_attn_fwd_capture", "sage_device_check"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -150,8 +151,11 @@ class SageQuant:
 
 
 def sage_quant_prep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: SageQuant | None = None,
-                    stream=None) -> SageQuant:
-    """K mean, K smoothing, INT8 Q/K per block and FP8 V per channel on the GPU."""
+                    stream=None, single_pass: bool = False) -> SageQuant:
+    """K mean, K smoothing, INT8 Q/K per block and FP8 V per channel on the GPU.
+
+    single_pass selects sage_quant_prep_single_pass (K and V read once; same
+    results)."""
     for t in (q, k, v):
         if t.dtype != torch.bfloat16 or not t.is_cuda:
             raise TypeError("q, k, v must be bfloat16 CUDA tensors")
@@ -163,8 +167,9 @@ def sage_quant_prep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Sage
     st = SageStrides()
     st.q, st.k, st.v = _strides3(q), _strides3(k), _strides3(v)
     qc = quant.c_struct()
-    _check(lib().sage_quant_prep(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(quant.shape),
-                                 ctypes.byref(st), ctypes.byref(qc), _stream_handle(stream)), "sage_quant_prep")
+    name = "sage_quant_prep_single_pass" if single_pass else "sage_quant_prep"
+    _check(getattr(lib(), name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(quant.shape),
+                                ctypes.byref(st), ctypes.byref(qc), _stream_handle(stream)), name)
     return quant
 
 

@@ -29,8 +29,8 @@ def header_functions():
 
 def test_exports_every_header_function(L):
     names = header_functions()
-    assert {"sage_quant_prep", "sage_attn_fwd", "sage_attn_fwd_capture", "sage_buffer_bytes",
-            "sage_status_string", "sage_device_check"} <= set(names)
+    assert {"sage_quant_prep", "sage_quant_prep_single_pass", "sage_attn_fwd", "sage_attn_fwd_capture",
+            "sage_buffer_bytes", "sage_status_string", "sage_device_check"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -74,12 +74,13 @@ def _strides(B, H, N, D):
     return st
 
 
-def test_prep_validation_before_any_hip_call(L):
+@pytest.mark.parametrize("entry", ["sage_quant_prep", "sage_quant_prep_single_pass"])
+def test_prep_validation_before_any_hip_call(L, entry):
     shape = sage.SageShape(1, 2, 100, 100, 64)
     st = _strides(1, 2, 100, 64)
     qc = _fake_quant()
     q, k, v = 1 << 36, 2 << 36, 3 << 36
-    call = lambda *a: L.sage_quant_prep(*a)
+    call = lambda *a: getattr(L, entry)(*a)
     assert call(q, k, v, None, ctypes.byref(st), ctypes.byref(qc), None) == -1
     assert call(None, k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(qc), None) == -1
     assert call(q, k, v, ctypes.byref(shape), ctypes.byref(st), None, None) == -1

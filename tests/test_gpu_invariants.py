@@ -82,11 +82,12 @@ def test_thousand_launches_bit_identical():
     assert int(mismatches) == 0
 
 
-def test_graph_capture_replay_matches_eager():
+@pytest.mark.parametrize("single_pass", [False, True])
+def test_graph_capture_replay_matches_eager(single_pass):
     w = WORKLOADS["ragged_tails"]
     q, k, v = make_inputs(w, seed=21, B=1, H=4, Nq=500, Nkv=700, D=128)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
-    quant = sage.sage_quant_prep(qd, kd, vd)
+    quant = sage.sage_quant_prep(qd, kd, vd, single_pass=single_pass)
     out = sage.sage_attn_fwd(quant)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -94,7 +95,7 @@ def test_graph_capture_replay_matches_eager():
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            sage.sage_quant_prep(qd, kd, vd, out=quant)
+            sage.sage_quant_prep(qd, kd, vd, out=quant, single_pass=single_pass)
             sage.sage_attn_fwd(quant, out=out)
     torch.cuda.current_stream().wait_stream(s)
     for r in range(4):

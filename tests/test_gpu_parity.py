@@ -52,7 +52,7 @@ def _bits32(x):
 class Run:
     """One prep + fwd (+ capture of sampled units) on the GPU, plus host copies."""
 
-    def __init__(self, q, k, v, units, sm_scale=None, strided=False):
+    def __init__(self, q, k, v, units, sm_scale=None, strided=False, single_pass=False):
         self.q, self.k, self.v = q, k, v
         self.B, self.H, self.Nq, self.D = q.shape
         self.Nkv = k.shape[2]
@@ -64,9 +64,9 @@ class Run:
             vd = v.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
         else:
             qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-        print("  gpu run B=%d H=%d Nq=%d Nkv=%d D=%d units=%d strided=%s"
-              % (self.B, self.H, self.Nq, self.Nkv, self.D, len(units), strided), flush=True)
-        self.quant = sage.sage_quant_prep(qd, kd, vd)
+        print("  gpu run B=%d H=%d Nq=%d Nkv=%d D=%d units=%d strided=%s single_pass=%s"
+              % (self.B, self.H, self.Nq, self.Nkv, self.D, len(units), strided, single_pass), flush=True)
+        self.quant = sage.sage_quant_prep(qd, kd, vd, single_pass=single_pass)
         self.out = sage.sage_attn_fwd(self.quant, sm_scale)
         self.units = list(units)
         oc, s_cap, p8_cap, md_cap = sage.sage_attn_fwd_capture(self.quant, self.units, sm_scale)
@@ -222,12 +222,32 @@ def test_single_tile_all_rows():
     stats.check()
 
 
-def test_ragged_tails_all_rows():
+def sync_words(run):
+    """Arrival counters, ready flags and status word of the single-pass prep
+    (the workspace's last region: after the FP64 column partials, the column
+    maxima and the V inverses, each 256-byte aligned)."""
+    BH, D = run.B * run.H, run.D
+    nchunk = -(-run.Nkv // 256)
+    a256 = lambda x: (x + 255) // 256 * 256
+    off = a256(BH * nchunk * D * 8) + a256(BH * nchunk * D * 4) + a256(BH * D * 4)
+    w = run.quant.workspace[off:off + 4 * (2 * BH + 1)].cpu().numpy().view(np.uint32)
+    return w[:BH], w[BH:2 * BH], int(w[2 * BH])
+
+
+def fused_groups(Nkv, D):
+    return -(-Nkv // (16 * 256 // (D // 8)))
+
+
+@pytest.mark.parametrize("single_pass", [False, True])
+def test_ragged_tails_all_rows(single_pass):
     w = WORKLOADS["ragged_tails"]
     q, k, v = make_inputs(w)
     nqb = 8
     units = list(range(8 * nqb))                # every unit of every head
-    run = Run(q, k, v, units)
+    run = Run(q, k, v, units, single_pass=single_pass)
+    if single_pass:
+        arrived, ready, status = sync_words(run)
+        assert status == 0 and np.all(arrived == fused_groups(w.Nkv, w.D)) and np.all(ready == 1)
     preps = {bh: run.oracle_prep(bh) for bh in range(8)}
     for bh, p in preps.items():
         check_prep_bh(run, bh, p)
@@ -250,19 +270,63 @@ def test_headdim64_full_size_sampled():
 
 # ---------------------------------------------------------------- edge cases --
 
+@pytest.mark.parametrize("single_pass", [False, True])
 @pytest.mark.parametrize("Nq,Nkv,D", [(1, 1, 64), (1, 1, 128), (129, 65, 64), (127, 63, 128),
-                                      (300, 1, 128), (5, 700, 64), (256, 128, 128)])
-def test_edge_shapes_all_rows(Nq, Nkv, D):
+                                      (300, 1, 128), (5, 700, 64), (256, 128, 128), (130, 4097, 128),
+                                      (70, 8191, 64)])
+def test_edge_shapes_all_rows(Nq, Nkv, D, single_pass):
     w = WORKLOADS["ragged_tails"]
     q, k, v = make_inputs(w, seed=7 + Nq + Nkv, B=2, H=2, Nq=Nq, Nkv=Nkv, D=D)
     nqb = -(-Nq // 128)
-    run = Run(q, k, v, list(range(4 * nqb)))
+    run = Run(q, k, v, list(range(4 * nqb)), single_pass=single_pass)
     preps = {bh: run.oracle_prep(bh) for bh in range(4)}
     for bh, p in preps.items():
         check_prep_bh(run, bh, p)
     stats = OStats()
     check_units(run, stats, preps)
     stats.check()
+
+
+@pytest.mark.parametrize("Nkv,D", [(66313, 128), (131405, 64)])
+def test_single_pass_entry_falls_back_for_long_keys(Nkv, D):
+    """Keys beyond the single pass's group limit take the three launches;
+    prep bit-exact, two 2-row units end to end."""
+    assert fused_groups(Nkv, D) > 256
+    w = WORKLOADS["ragged_tails"]
+    q, k, v = make_inputs(w, seed=11 + D, B=1, H=2, Nq=130, Nkv=Nkv, D=D)
+    run = Run(q, k, v, [1, 3], single_pass=True)
+    preps = {bh: run.oracle_prep(bh) for bh in range(2)}
+    for bh, p in preps.items():
+        check_prep_bh(run, bh, p)
+    stats = OStats()
+    check_units(run, stats, preps)
+    stats.check()
+
+
+def test_single_pass_prep_full_size_bit_identical():
+    """The single pass gives the three launches' bytes on the full-size
+    workloads; every head counted all its groups in, and no wait expired."""
+    for name in ("dit_block", "long_video", "headdim64"):
+        w = WORKLOADS[name]
+        q, k, v = make_inputs(w)
+        dev = torch.device("cuda:0")
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        ref = sage.sage_quant_prep(qd, kd, vd)
+        quant = sage.sage_quant_prep(qd, kd, vd, single_pass=True)
+        torch.cuda.synchronize()
+        for f in ("q_codes", "q_scale", "k_codes", "k_scale", "v_codes", "v_scale", "k_mean"):
+            assert torch.equal(getattr(ref, f).view(torch.uint8), getattr(quant, f).view(torch.uint8)), (name, f)
+
+        class R:
+            pass
+        r = R()
+        r.B, r.H, r.Nkv, r.D, r.quant = w.B, w.H, w.Nkv, w.D, quant
+        arrived, ready, status = sync_words(r)
+        assert status == 0, name
+        assert np.all(arrived == fused_groups(w.Nkv, w.D)), name
+        assert np.all(ready == 1), name
+        del quant, ref, qd, kd, vd
+        torch.cuda.empty_cache()
 
 
 def test_strided_nhd_inputs_and_custom_scale():
@@ -300,9 +364,15 @@ def test_repeat_launches_bit_identical():
     quant = sage.sage_quant_prep(qd, kd, vd)
     first = sage.sage_attn_fwd(quant).clone()
     codes = quant.k_codes.clone(), quant.v_codes.clone()
-    for _ in range(200):
-        sage.sage_quant_prep(qd, kd, vd, out=quant)
+    for i in range(200):
+        # alternate the two prep entries: the single pass's in-launch waits and
+        # its arrival counters are cleared and reused on every call
+        sage.sage_quant_prep(qd, kd, vd, out=quant, single_pass=bool(i & 1))
         o = sage.sage_attn_fwd(quant)
+        if i % 50 == 49:
+            torch.cuda.synchronize()
+            assert torch.equal(o.view(torch.int16), first.view(torch.int16)), i
+            assert torch.equal(quant.k_codes, codes[0]) and torch.equal(quant.v_codes, codes[1]), i
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), first.view(torch.int16))
     assert torch.equal(quant.k_codes, codes[0]) and torch.equal(quant.v_codes, codes[1])
