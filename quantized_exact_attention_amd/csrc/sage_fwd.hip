@@ -54,6 +54,15 @@ __device__ __forceinline__ float partner_sum(float x) {
 // few values that do not fit are spilled outside the tile loop only).
 template <int D> struct FwdOccupancy { static constexpr int waves_per_simd = D == 128 ? 3 : 4; };
 
+// Masking of the ragged last tile: lane l holds keys kb*32 + 8*(v/4) + 4*(l/32)
+// + v%4, so key (kb, v) is past Nkv iff kb*32 + 8*(v/4) + v%4 >= kvalid -
+// 4*(l/32).  The lane id is recomputed here (from the exec mask) so that no
+// register carries it through the traversal.
+__device__ __forceinline__ int masked_key_limit(int kvalid) {
+  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return kvalid - 4 * (lane >> 5);
+}
+
 // log2(448): P is produced directly as 448 * 2^(s - m) = 2^(s - m + log2 448).
 constexpr float kLog2_448 = 8.80735492205760410744f;
 
@@ -124,11 +133,12 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   const int kvalid = p.Nkv - j * kBK;
   const bool masked = kvalid < kBK;
   if (masked) {
+    const int klim = masked_key_limit(kvalid);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        if (kb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3) >= kvalid) sacc[kb][v] = INT_MIN;
+        if (kb * 32 + 8 * (v >> 2) + (v & 3) >= klim) sacc[kb][v] = INT_MIN;
   }
 
   // ---- online softmax; max in the integer domain (the per-tile factor is >= 0) ----
@@ -154,11 +164,12 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
 #pragma unroll
     for (int v = 0; v < 16; ++v) pv[kb][v] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sacc[kb][v], c, nb));
   if (masked) {
+    const int klim = masked_key_limit(kvalid);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        if (kb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3) >= kvalid) pv[kb][v] = 0.f;
+        if (kb * 32 + 8 * (v >> 2) + (v & 3) >= klim) pv[kb][v] = 0.f;
   }
   // row sum as a tree (short dependency chains)
   float s8[8];
