@@ -84,9 +84,9 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         "unit": "TFLOPS",
         "cores": 1,
         "kind": "oracle",
-        "sample": "prep of 1 of %d heads (%.2f s) + %d of %d 128-row Q blocks of that head (%.2f s), "
-                  "extrapolated linearly to the whole workload (%.0f s)" % (BH, t_prep, blocks, BH * nqb,
-                                                                           t_att, t_total),
+        "sample": "prep of head (0,0) of %d heads (%.2f s) + %d of that head's %d 128-row Q blocks "
+                  "(%.2f s), single thread; extrapolated linearly to %d heads x %d blocks (%.0f s)"
+                  % (BH, t_prep, blocks, nqb, t_att, BH, nqb, t_total),
     }
 
 
