@@ -87,7 +87,9 @@ __device__ __forceinline__ void issue_tile(uint8_t *dst, const int8_t *kg, const
     const int c = i * 4 + wave;
     const uint8_t *src = i < NLD / 2 ? (const uint8_t *)kg + (size_t)t * TILE + c * 1024
                                      : vg + (size_t)t * TILE + (c - TILE / 1024) * 1024;
-    __builtin_amdgcn_global_load_lds((glb_void_t *)(src + lane * 16), (lds_void_t *)(dst + c * 1024), 16, 0, 0);
+    // uniform base + 32-bit lane offset: the scalar-base form of the copy
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(src + (uint32_t)lane * 16u), (lds_void_t *)(dst + c * 1024), 16, 0,
+                                     0);
   }
 }
 
@@ -109,8 +111,8 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   const int T = p.T;
   const int hi = lane >> 5;   // which 4-key group of each 8 this lane holds
   if (j + 1 < T) issue_tile<D>(nxt, kg, vg, j + 1, wave, lane);
-  const uint8_t *kl = cur;
-  const uint8_t *vl = cur + TILE;
+  const uint8_t *kl = cur + lane * 16;        // this lane's 16 bytes of every 1 KiB operand block
+  const uint8_t *vl = kl + TILE;
 
   // ---- S^T = K_j . Q^T (int32, exact) ----
   v16i sacc[2];
@@ -118,7 +120,7 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   for (int s = 0; s < NS; ++s) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const v4i a = *(const v4i *)(kl + (kb * NS + s) * 1024 + lane * 16);
+      const v4i a = *(const v4i *)(kl + (kb * NS + s) * 1024);
       sacc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[s], s == 0 ? (v16i){} : sacc[kb], 0, 0, 0);
     }
   }
@@ -155,7 +157,7 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   int mx = max(max(max(m4a, m4b), m4c), m4d);
   mx = partner_max(mx);
   const float c = (sq * load_uniform(ksc + j)) * p.sl2;   // fp32(fp32(sq * sk_j) * sl2)
-  const float mnew = fmaxf(st.m, (float)mx * c);
+  const float mnew = __builtin_amdgcn_fmed3f(st.m, (float)mx * c, INFINITY);   // max; no NaN here
   const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);   // "rescale"; 0 on the first tile
   const float nb = kLog2_448 - mnew;
   float pv[2][16];
@@ -215,8 +217,8 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   v16f part[NS];
 #pragma unroll
   for (int cb = 0; cb < NS; ++cb) {
-    const v4i a0 = *(const v4i *)(vl + (cb * 2 + 0) * 1024 + lane * 16);
-    const v4i a1 = *(const v4i *)(vl + (cb * 2 + 1) * 1024 + lane * 16);
+    const v4i a0 = *(const v4i *)(vl + (cb * 2 + 0) * 1024);
+    const v4i a1 = *(const v4i *)(vl + (cb * 2 + 1) * 1024);
     const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     part[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pop, zero16, 0, 0, 0, 0, 0, 0);
   }
