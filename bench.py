@@ -79,11 +79,18 @@ def cpu_baseline(w, q, k, v, budget_s: float):
             blocks += 1
     BH = w.B * w.H
     t_total = t_prep * BH + (t_att / blocks) * BH * nqb
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {
         "value": w.flops / t_total / 1e12,
         "unit": "TFLOPS",
         "cores": 1,
         "kind": "oracle",
+        "host": {"cpu_model": cpu_model, "cores_available": len(os.sched_getaffinity(0))},
         "sample": "prep of head (0,0) of %d heads (%.2f s) + %d of that head's %d 128-row Q blocks "
                   "(%.2f s), single thread; extrapolated linearly to %d heads x %d blocks (%.0f s)"
                   % (BH, t_prep, blocks, nqb, t_att, BH, nqb, t_total),
@@ -94,7 +101,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_video")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention to time")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -49,15 +49,15 @@ __device__ __forceinline__ float partner_sum(float x) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Waves per SIMD: 3 at D = 128 (168 VGPRs per lane, which the per-wave state
-// RO 64, S/p 32, P8 8, Q 16, partial 16-64 fits), 4 at D = 64 (128 VGPRs; the
-// few values that do not fit are spilled outside the tile loop only).
+// Waves per SIMD: 3 at D = 128 (at most 168 VGPRs per lane for the per-wave
+// state RO 64, S/p 32, P8 8, Q 16, partials up to 64; the kernel uses 168 with
+// no scratch), 4 at D = 64 (at most 128; it uses 97).
 template <int D> struct FwdOccupancy { static constexpr int waves_per_simd = D == 128 ? 3 : 4; };
 
 // Masking of the ragged last tile: lane l holds keys kb*32 + 8*(v/4) + 4*(l/32)
 // + v%4, so key (kb, v) is past Nkv iff kb*32 + 8*(v/4) + v%4 >= kvalid -
-// 4*(l/32).  The lane id is recomputed here (from the exec mask) so that no
-// register carries it through the traversal.
+// 4*(l/32).  The lane id is recomputed here (v_mbcnt) so that no register
+// carries it, or the 32 key indices, through the traversal.
 __device__ __forceinline__ int masked_key_limit(int kvalid) {
   const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   return kvalid - 4 * (lane >> 5);
@@ -87,9 +87,7 @@ __device__ __forceinline__ void issue_tile(uint8_t *dst, const int8_t *kg, const
     const int c = i * 4 + wave;
     const uint8_t *src = i < NLD / 2 ? (const uint8_t *)kg + (size_t)t * TILE + c * 1024
                                      : vg + (size_t)t * TILE + (c - TILE / 1024) * 1024;
-    // uniform base + 32-bit lane offset: the scalar-base form of the copy
-    __builtin_amdgcn_global_load_lds((glb_void_t *)(src + (uint32_t)lane * 16u), (lds_void_t *)(dst + c * 1024), 16, 0,
-                                     0);
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(src + lane * 16), (lds_void_t *)(dst + c * 1024), 16, 0, 0);
   }
 }
 
