@@ -77,7 +77,12 @@ typedef struct sage_strides {
  *           [channel = 32c + L%32] quantized with the channel scale.
  *  v_scale  float [B,H,D]: per-channel absmax/448 over all Nkv keys.
  *  k_mean   float [B,H,D]: per-channel mean of K over all Nkv keys.
- *  workspace  scratch for the prep statistics (sage_buffer_bytes).
+ *  workspace  scratch of the prep (sage_buffer_bytes): column partials of the
+ *           K sums and V maxima, V inverses and, for the single pass, per-(b,h)
+ *           arrival counters and ready flags and one status word.  Its
+ *           contents before a call do not matter (each call initializes what
+ *           it reads); two prep calls must not use one workspace at the same
+ *           time.
  */
 typedef struct sage_quant {
   int8_t *q_codes;
