@@ -9,6 +9,7 @@ smoothing leaves softmax unchanged, scale equivariance, permutation
 equivariance); special cases with known answers (one key, constant K).
 """
 
+import math
 import os
 from fractions import Fraction
 
@@ -30,6 +31,11 @@ def bf16_exact(shape, rng, scale=1.0):
     """float32 array of values exactly representable in bfloat16."""
     t = torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32))
     return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def textbook_scale(d):
+    """The usual attention scale 1/sqrt(D), computed here, not by the oracle."""
+    return 1.0 / math.sqrt(d)
 
 
 def softmax_attention_f64(q, k, v, sm_scale):
@@ -223,9 +229,16 @@ def test_online_equals_two_pass_without_quantization(nq, nkv, d):
     assert np.allclose(got, ref, rtol=2**-8, atol=1e-5)
 
 
+def test_default_softmax_scale_literal():
+    """Reading of the silent scale: 1/sqrt(D), rounded once to float32."""
+    assert so.default_sm_scale(64) == np.float32(0.125)
+    assert so.default_sm_scale(128) == np.float32(0.08838834764831845)
+    assert so.default_sm_scale(128).dtype == np.float32
+
+
 def test_k_smoothing_invariance_f64():
     q, k, v = _tiny(40, 150, 64, 31)
-    sm = float(so.default_sm_scale(64))
+    sm = textbook_scale(64)
     mean = k.astype(np.float64).mean(axis=0)
     a = softmax_attention_f64(q, k, v, sm)
     b = softmax_attention_f64(q, k - mean, v, sm)
@@ -246,7 +259,7 @@ def test_quantized_pipeline_cosine_vs_f64(nq, nkv, d, outlier, bound):
     q, k, v = _tiny(nq, nkv, d, 40 + nkv, outlier=outlier)
     p = so.prep_bh(q, k, v)
     o = so.bf16_bits_to_f32(so.attention_rows(p)).astype(np.float64).ravel()
-    ref = softmax_attention_f64(q, k, v, float(so.default_sm_scale(d))).ravel()
+    ref = softmax_attention_f64(q, k, v, textbook_scale(d)).ravel()
     cos = o @ ref / np.linalg.norm(o) / np.linalg.norm(ref)
     assert cos >= bound, cos
 
@@ -337,7 +350,7 @@ def test_single_tile_workload_end_to_end():
     p = so.prep_bh(q, k, v)
     O, ck = so.attention_rows(p, want_checkpoints=True)
     assert O.shape == (128, 128) and ck.S.shape == (128, 192) and ck.m.shape == (128, 3)
-    ref = softmax_attention_f64(q, k, v, float(so.default_sm_scale(128)))
+    ref = softmax_attention_f64(q, k, v, textbook_scale(128))
     o = so.bf16_bits_to_f32(O).astype(np.float64)
     cos = (o.ravel() @ ref.ravel()) / np.linalg.norm(o) / np.linalg.norm(ref)
     assert cos >= 0.999
