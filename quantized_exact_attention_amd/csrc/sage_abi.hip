@@ -61,7 +61,7 @@ size_t buffer_bytes(const sage_shape_t *s, int which) {
     case SAGE_BUF_K_MEAN: return BH * s->D * sizeof(float);
     case SAGE_BUF_WORKSPACE:
       return align256(ws_ksum_bytes((int)BH, nchunk, s->D)) + align256(ws_vmax_bytes((int)BH, nchunk, s->D)) +
-             align256(ws_vinv_bytes((int)BH, s->D)) + align256(ws_sync_bytes((int)BH));
+             align256(ws_vinv_bytes((int)BH, s->D)) + align256(ws_sync_bytes((int)BH, s->D));
     default: return 0;
   }
 }
@@ -218,6 +218,8 @@ int quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *
   p.ws_vinv = (float *)ws;
   ws += align256(ws_vinv_bytes(BH, s->D));
   p.ws_sync = (uint32_t *)ws;
+  p.ws_asum = (double *)(p.ws_sync + ws_sync_head_words(BH));
+  p.ws_amax = (uint32_t *)(p.ws_asum + (size_t)BH * s->D);
   const int groups = ceil_div(s->Nkv, kFusedRows(s->D));
   // G = 0: statistics, finalize and quantization launches
   p.G = single_pass && groups <= kFusedMaxGroups ? groups : 0;

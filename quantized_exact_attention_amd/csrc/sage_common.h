@@ -34,6 +34,8 @@ struct PrepParams {
   float *ws_vmax;                 // [B*H][nchunk][D]
   float *ws_vinv;                 // [B*H][D]
   uint32_t *ws_sync;              // single-pass path: [B*H] arrivals, [B*H] ready flags, 1 status word
+  double *ws_asum;                // single-pass path: [B*H][D] K column sums (atomic, exact)
+  uint32_t *ws_amax;              // single-pass path: [B*H][D] V column max |v| (float bits, atomic max)
   int G;                          // single-pass path: K/V workgroups per (b,h); 0 selects three launches
 };
 
@@ -60,7 +62,12 @@ struct FwdParams {
 inline size_t ws_ksum_bytes(int BH, int nchunk, int D) { return (size_t)BH * nchunk * D * sizeof(double); }
 inline size_t ws_vmax_bytes(int BH, int nchunk, int D) { return (size_t)BH * nchunk * D * sizeof(float); }
 inline size_t ws_vinv_bytes(int BH, int D) { return (size_t)BH * D * sizeof(float); }
-inline size_t ws_sync_bytes(int BH) { return ((size_t)2 * BH + 1) * sizeof(uint32_t); }
+// Single-pass region, cleared as 32-bit words before every single-pass call:
+// arrivals, ready flags, status word, then (8-byte aligned) the column sums and
+// column maxima.
+inline size_t ws_sync_head_words(int BH) { return ((size_t)2 * BH + 2) & ~(size_t)1; }
+inline size_t ws_sync_words(int BH, int D) { return ws_sync_head_words(BH) + (size_t)BH * D * 3; }
+inline size_t ws_sync_bytes(int BH, int D) { return ws_sync_words(BH, D) * sizeof(uint32_t); }
 
 // Single-pass prep: one workgroup holds kFusedRows(D) K and V rows in registers
 // (16 per thread); used while a head needs at most kFusedMaxGroups workgroups.

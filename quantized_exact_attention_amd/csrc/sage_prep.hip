@@ -285,11 +285,12 @@ __device__ __forceinline__ void quant_kv_tile(const PrepParams &p, int j, int bh
 }
 
 // ---- single pass: K and V read from HBM once ----------------------------------
-// Workgroup (b,h, g) keeps rows [g*R, g*R + R) of K and V in registers, writes
-// their column partials and counts itself in; the last workgroup of the head
-// reduces the partials (K mean, V scale and inverse) and raises the head's
-// flag; every workgroup of the head waits for the flag, then quantizes its
-// rows.  The Q blocks take the grid's last workgroups.  Workgroups are
+// Workgroup (b,h, g) keeps rows [g*R, g*R + R) of K and V in registers, adds
+// its column sums and maxima into the head's accumulators (atomics: the sums
+// are exact, so their order does not matter) and counts itself in; the last
+// workgroup of the head turns the totals into the K mean, V scale and inverse
+// and raises the head's flag; every workgroup of the head waits for the flag, then quantizes its
+// rows; the head's Q blocks follow its groups in the grid.  Workgroups are
 // dispatched in index order and a head needs at most kFusedMaxGroups of them,
 // far fewer than fit on the device at once, so the workgroups of a head are
 // all resident before any waits for long; the wait is still bounded, and on
@@ -325,8 +326,6 @@ struct FusedSmem {
     uint16_t tile[kBK][D + 8];
   } u;
   float red[kFusedRows(D) / kBK][4];
-  double fsum[256 / D][D];
-  float fmax[256 / D][D];
   int last;
 };
 
@@ -376,11 +375,12 @@ __device__ __forceinline__ void fused_kv_group(const PrepParams &p, int bh, int 
     double s = 0.0;
     float mx = 0.f;
     for (int i = 0; i < TL; ++i) { s += sm.u.st.sum[i][c]; mx = fmaxf(mx, sm.u.st.max[i][c]); }
-    const size_t o = ((size_t)bh * p.nchunk + g) * D + c;
-    coherent_store(p.ws_ksum + o, s);
-    coherent_store(p.ws_vmax + o, mx);
+    // exact partial sums: the atomic additions give the exact total in any order
+    __hip_atomic_fetch_add(p.ws_asum + (size_t)bh * D + c, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_max(p.ws_amax + (size_t)bh * D + c, __float_as_uint(mx), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);   // max |v| >= 0: bit order is value order
   }
-  completed_barrier();                           // every partial of the group has reached memory
+  completed_barrier();                           // every update of the group has completed
   uint32_t *arrived = p.ws_sync + bh, *ready = p.ws_sync + p.B * p.H + bh, *status = p.ws_sync + 2 * p.B * p.H;
   if (tid == 0)
     sm.last = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(p.G - 1);
@@ -388,34 +388,9 @@ __device__ __forceinline__ void fused_kv_group(const PrepParams &p, int bh, int 
 
   // ---- the last group of the head: K mean, V scale and inverse ----
   if (sm.last) {
-    constexpr int NG = 256 / D;
-    const int c = tid % D, gi = tid / D;
-    double s = 0.0;
-    float mx = 0.f;
-    constexpr int U = 8;
-    for (int i0 = gi; i0 < p.G; i0 += NG * U) {
-      double ps[U];
-      float pm[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * NG;
-        ps[u] = 0.0;
-        pm[u] = 0.f;
-        if (i < p.G) {
-          const size_t o = ((size_t)bh * p.nchunk + i) * D + c;
-          ps[u] = coherent_load(p.ws_ksum + o);
-          pm[u] = coherent_load(p.ws_vmax + o);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) { s += ps[u]; mx = fmaxf(mx, pm[u]); }   // exact sums: any order
-    }
-    sm.fsum[gi][c] = s;
-    sm.fmax[gi][c] = mx;
-    __syncthreads();
-    if (gi == 0) {
-#pragma unroll
-      for (int i = 1; i < NG; ++i) { s += sm.fsum[i][c]; mx = fmaxf(mx, sm.fmax[i][c]); }
+    for (int c = tid; c < D; c += 256) {
+      const double s = coherent_load(p.ws_asum + (size_t)bh * D + c);
+      const float mx = __uint_as_float(coherent_load(p.ws_amax + (size_t)bh * D + c));
       coherent_store(p.k_mean + bh * D + c, (float)(s / (double)p.Nkv));   // FP64 quotient, one rounding
       p.v_scale[bh * D + c] = mx > 0.f ? mx / 448.0f : 0.f;
       coherent_store(p.ws_vinv + bh * D + c, mx > 0.f ? 448.0f / mx : 0.f);
@@ -522,17 +497,15 @@ __device__ __forceinline__ void fused_kv_group(const PrepParams &p, int bh, int 
   }
 }
 
+// Workgroup order, head by head: the head's G K/V groups, then its Q blocks,
+// whose loads keep memory busy while the head's groups wait for each other.
 template <int D>
 __global__ __launch_bounds__(256) void k_prep_fused(PrepParams p) {
   __shared__ FusedSmem<D> sm;
-  const int nkv = p.B * p.H * p.G;
-  if ((int)blockIdx.x < nkv) {
-    const int bh = blockIdx.x / p.G;
-    fused_kv_group<D>(p, bh, blockIdx.x - bh * p.G, sm);
-  } else {
-    const int qi = blockIdx.x - nkv, bh = qi / p.nqb;
-    quant_q_block<D>(p, qi - bh * p.nqb, bh, &sm.red[0][0]);
-  }
+  const int per = p.G + p.nqb;
+  const int bh = blockIdx.x / per, r = blockIdx.x - bh * per;
+  if (r < p.G) fused_kv_group<D>(p, bh, r, sm);
+  else quant_q_block<D>(p, r - p.G, bh, &sm.red[0][0]);
 }
 
 // Zero the arrival counters, ready flags and status word of the single pass.
@@ -562,7 +535,7 @@ template <int D>
 static hipError_t launch_prep_d(const PrepParams &p, hipStream_t st) {
   const int BH = p.B * p.H;
   if (p.G > 0) {
-    const int nsync = 2 * BH + 1;
+    const int nsync = (int)ws_sync_words(BH, D);
     hipLaunchKernelGGL(k_prep_clear, dim3((nsync + 255) / 256), dim3(256), 0, st, p.ws_sync, nsync);
     hipLaunchKernelGGL(k_prep_fused<D>, dim3(BH * p.G + BH * p.nqb), dim3(256), 0, st, p);
     return hipGetLastError();
