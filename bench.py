@@ -189,6 +189,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    # SHA-256 of the forward's BF16 output bytes (deterministic across launches)
+    res["output_sha256"] = hashlib.sha256(out.view(torch.int16).cpu().numpy().tobytes()).hexdigest()
     # The single-pass prep entry (K and V read once), timed apart from the step.
     sp_ms = []
     for i in range(args.warmup + args.steps):
