@@ -4,8 +4,11 @@
 // smoothing, INT8 quantization, FP8 V" of the contract imported in
 // "Experiment Log", Phase 0 Import And Verification.
 //
-// All passes are HBM-bound streaming kernels: 16-byte loads along the
-// contiguous channel dimension, 16-byte code stores.
+// Every kernel here is an HBM-bound stream: 16-byte loads along the contiguous
+// channel dimension, code stores of 8 (Q, K) or 16 (V) bytes in operand order.
+// Two schedules: three launches ([statistics | Q] -> finalize -> [K, V per
+// tile]), which read K and V twice, and a single pass that reads them once
+// (sections 1-4 and 5 below).
 #include "sage_common.h"
 
 namespace sage {
@@ -284,7 +287,7 @@ __device__ __forceinline__ void quant_kv_tile(const PrepParams &p, int j, int bh
   }
 }
 
-// ---- single pass: K and V read from HBM once ----------------------------------
+// ---- 5. single pass: K and V read from HBM once -------------------------------
 // Workgroup (b,h, g) keeps rows [g*R, g*R + R) of K and V in registers, adds
 // its column sums and maxima into the head's accumulators (atomics: the sums
 // are exact, so their order does not matter) and counts itself in; the last
