@@ -329,6 +329,35 @@ def test_single_pass_prep_full_size_bit_identical():
         torch.cuda.empty_cache()
 
 
+def _random_cases(n=24):
+    rng = np.random.default_rng(2024)
+    cases = []
+    for i in range(n):
+        D = int(rng.choice([64, 128]))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        Nq, Nkv = int(rng.integers(1, 700)), int(rng.integers(1, 700))
+        dist = str(rng.choice(["dit_block", "ragged_tails", "headdim64"]))   # no / 3% / 1% outliers
+        sm = None if rng.random() < 0.7 else float(rng.uniform(0.02, 0.3))
+        strided = bool(rng.random() < 0.3)
+        cases.append((i, dist, B, H, Nq, Nkv, D, sm, strided, bool(i & 1)))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: "r%d_%s_%dx%dx%dx%dx%d" % (c[0], c[1], *c[2:7]))
+def test_random_shapes_all_rows(case):
+    """Seeded random shapes, scales, input layouts and prep entries; every row."""
+    i, dist, B, H, Nq, Nkv, D, sm, strided, single = case
+    q, k, v = make_inputs(WORKLOADS[dist], seed=5000 + i, B=B, H=H, Nq=Nq, Nkv=Nkv, D=D)
+    nqb = -(-Nq // 128)
+    run = Run(q, k, v, list(range(B * H * nqb)), sm_scale=sm, strided=strided, single_pass=single)
+    preps = {bh: run.oracle_prep(bh) for bh in range(B * H)}
+    for bh, p in preps.items():
+        check_prep_bh(run, bh, p)
+    stats = OStats()
+    check_units(run, stats, preps)
+    stats.check()
+
+
 def test_strided_nhd_inputs_and_custom_scale():
     w = WORKLOADS["ragged_tails"]
     q, k, v = make_inputs(w, seed=99, B=1, H=3, Nq=200, Nkv=300, D=128)
