@@ -135,10 +135,13 @@ int sage_quant_prep(const void *q, const void *k, const void *v, const sage_shap
  * sage_quant_prep), ownership and errors as for sage_quant_prep.  Used while a
  * (b,h) needs at most 256 such workgroups (Nkv <= 65536 at D = 128, <= 131072 at
  * D = 64); longer keys take sage_quant_prep's three launches.  Launches 2
- * kernels on `stream`.  Its workgroups wait for each other inside the launch;
- * the wait is bounded, and a wait that ran out leaves a nonzero status word in
- * the workspace (never observed: the workgroups of a head are resident
- * together).  Slower than sage_quant_prep on the shapes measured so far.
+ * kernels on `stream`.  Its workgroups wait for each other inside the launch:
+ * this relies on a head's workgroups all becoming resident, so do not run it
+ * concurrently (other streams) with another single-pass prep or with kernels
+ * that hold compute units indefinitely.  The wait is bounded (~0.1 s); one that
+ * ran out leaves a nonzero status word in the workspace and the outputs of that
+ * call are invalid (never observed in the tests, which check the word).  About
+ * as fast as sage_quant_prep on the shapes measured so far.
  */
 int sage_quant_prep_single_pass(const void *q, const void *k, const void *v, const sage_shape_t *shape,
                                 const sage_strides_t *strides, const sage_quant_t *quant, void *stream);
