@@ -100,7 +100,8 @@ def cpu_baseline(w, q, k, v, budget_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 20, or 100 for workloads under 1 TFLOP)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_video")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention to time")
@@ -110,7 +111,7 @@ def main():
                          "HBM traffic, used to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)"
+        print("bench.py measures one GPU only: the path runs on a single GPU (requested --gpus %d)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -123,6 +124,8 @@ def main():
     if not os.path.exists(qbuild.LIB_PATH):
         qbuild.build()
     w = WORKLOADS[args.workload]
+    if args.steps is None:
+        args.steps = 100 if w.flops < 1e12 else 20
     print("bench: generating %s inputs B=%d H=%d Nq=%d Nkv=%d D=%d" % (w.name, w.B, w.H, w.Nq, w.Nkv, w.D),
           file=sys.stderr, flush=True)
     q, k, v = make_inputs(w)
@@ -175,6 +178,8 @@ def main():
         "pct_of_peak": 100.0 * (w.flops / (ms_per_step * 1e-3) / 1e12) / MFMA_PEAK_TFLOPS,
         "step_ms_p50": statistics.median(step_ms),
         "step_ms_cv": statistics.pstdev(step_ms) / statistics.mean(step_ms),
+        "step_ms_p10": statistics.quantiles(step_ms, n=10)[0] if len(step_ms) > 1 else step_ms[0],
+        "step_ms_p90": statistics.quantiles(step_ms, n=10)[-1] if len(step_ms) > 1 else step_ms[0],
         "prep_ms_p50": statistics.median(prep_ms),
         "fwd_ms_p50": statistics.median(fwd_ms),
         "fwd_tflops_p50": w.flops / (statistics.median(fwd_ms) * 1e-3) / 1e12,
