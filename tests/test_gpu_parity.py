@@ -305,10 +305,15 @@ def test_single_pass_entry_falls_back_for_long_keys(Nkv, D):
 
 def test_single_pass_prep_full_size_bit_identical():
     """The single pass gives the three launches' bytes on the full-size
-    workloads; every head counted all its groups in, and no wait expired."""
-    for name in ("dit_block", "long_video", "headdim64"):
+    workloads, on 256 heads at once and at the group limit (256 groups for one
+    head); every head counted all its groups in, and no wait expired."""
+    cases = [("dit_block", {}), ("long_video", {}), ("headdim64", {}),
+             ("dit_block", dict(B=8, H=32, Nq=1024, Nkv=8192, D=64)),
+             ("dit_block", dict(B=1, H=1, Nq=300, Nkv=65536, D=128))]
+    for name, over in cases:
         w = WORKLOADS[name]
-        q, k, v = make_inputs(w)
+        q, k, v = make_inputs(w, **over)
+        print("  single pass vs three launches:", name, tuple(q.shape), tuple(k.shape), flush=True)
         dev = torch.device("cuda:0")
         qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
         ref = sage.sage_quant_prep(qd, kd, vd)
@@ -320,10 +325,12 @@ def test_single_pass_prep_full_size_bit_identical():
         class R:
             pass
         r = R()
-        r.B, r.H, r.Nkv, r.D, r.quant = w.B, w.H, w.Nkv, w.D, quant
+        r.B, r.H, _, r.D = q.shape
+        r.Nkv, r.quant = k.shape[2], quant
+        assert fused_groups(r.Nkv, r.D) <= 256
         arrived, ready, status = sync_words(r)
         assert status == 0, name
-        assert np.all(arrived == fused_groups(w.Nkv, w.D)), name
+        assert np.all(arrived == fused_groups(r.Nkv, r.D)), name
         assert np.all(ready == 1), name
         del quant, ref, qd, kd, vd
         torch.cuda.empty_cache()
