@@ -48,12 +48,36 @@ def measured_traffic(workload: str):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, budget_s: float):
+def _oracle_blocks(args):
+    """Worker: time the oracle's attention over the given 128-row Q blocks of
+    one head (single-threaded numpy in its own process)."""
+    prep, nq, blocks, budget_s = args
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import sage_oracle as so
+
+    done, t_att = 0, 0.0
+    with threadpool_limits(limits=1):
+        for qb in blocks:
+            if t_att >= budget_s:
+                break
+            rows = np.arange(qb * 128, min(nq, qb * 128 + 128))
+            t0 = time.perf_counter()
+            so.attention_rows(prep, rows)
+            t_att += time.perf_counter() - t0
+            done += 1
+    return done, t_att
+
+
+def cpu_baseline(w, q, k, v, budget_s: float, workers: int):
     """Time the oracle on a bounded sample and scale to effective TFLOPS.
 
-    Sample: the prep of head (0,0) plus as many 128-row Q blocks of that head
-    as fit in the budget; the full-workload time is extrapolated linearly
-    (prep per head x B*H, attention per block x B*H*ceil(Nq/128)).
+    Sample: the prep of head (0,0) plus 128-row Q blocks of that head in a
+    seeded random order, spread over `workers` processes (one thread each) for
+    about `budget_s` seconds each; the full-workload time is extrapolated
+    linearly (prep per head x B*H, attention per block x B*H*ceil(Nq/128)) and
+    divided by the number of workers.
     """
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -65,20 +89,30 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         t0 = time.perf_counter()
         p = so.prep_bh(qh, kh, vh)
         t_prep = time.perf_counter() - t0
-        nqb = -(-w.Nq // 128)
-        blocks = 0
-        t_att = 0.0
-        rng = np.random.default_rng(0)
-        order = rng.permutation(nqb)
-        while t_att < budget_s and blocks < nqb:
-            qb = int(order[blocks])
-            rows = np.arange(qb * 128, min(w.Nq, qb * 128 + 128))
-            t0 = time.perf_counter()
-            so.attention_rows(p, rows)
-            t_att += time.perf_counter() - t0
-            blocks += 1
+    nqb = -(-w.Nq // 128)
+    order = [int(x) for x in np.random.default_rng(0).permutation(nqb)]
+    workers = max(1, min(workers, nqb))
+    chunks = [order[i::workers] for i in range(workers)]
+    results = None
+    if workers > 1:
+        try:
+            import multiprocessing as mp
+            from concurrent.futures import ProcessPoolExecutor
+            # spawned children import numpy and the oracle only; a child that
+            # dies breaks the pool (an exception) rather than being respawned
+            with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as ex:
+                futs = [ex.submit(_oracle_blocks, (p, w.Nq, c, budget_s)) for c in chunks]
+                results = [f.result(timeout=4 * budget_s + 120) for f in futs]
+        except Exception as e:                  # fall back to one thread in this process
+            print("bench: oracle worker pool failed (%s); timing one thread" % e, file=sys.stderr, flush=True)
+            workers, chunks = 1, [order]
+    if results is None:
+        results = [_oracle_blocks((p, w.Nq, chunks[0], budget_s))]
+    blocks = sum(r[0] for r in results)
+    t_att = sum(r[1] for r in results)          # core-seconds
     BH = w.B * w.H
-    t_total = t_prep * BH + (t_att / blocks) * BH * nqb
+    t_core = t_prep * BH + (t_att / blocks) * BH * nqb
+    t_total = t_core / workers
     cpu_model = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
@@ -88,12 +122,13 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     return {
         "value": w.flops / t_total / 1e12,
         "unit": "TFLOPS",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
         "host": {"cpu_model": cpu_model, "cores_available": len(os.sched_getaffinity(0))},
         "sample": "prep of head (0,0) of %d heads (%.2f s) + %d of that head's %d 128-row Q blocks "
-                  "(%.2f s), single thread; extrapolated linearly to %d heads x %d blocks (%.0f s)"
-                  % (BH, t_prep, blocks, nqb, t_att, BH, nqb, t_total),
+                  "(%.1f core-s over %d single-threaded processes); extrapolated linearly to %d heads x %d "
+                  "blocks: %.0f core-s, %.1f s on %d cores" % (BH, t_prep, blocks, nqb, t_att, workers, BH, nqb,
+                                                             t_core, t_total, workers),
     }
 
 
@@ -104,7 +139,10 @@ def main():
                     help="timed steps (default: 20, or 100 for workloads under 1 TFLOP)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_video")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention to time")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle attention to time per worker process")
+    ap.add_argument("--cpu-workers", type=int, default=min(16, len(os.sched_getaffinity(0))),
+                    help="single-threaded oracle processes (independent Q blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a kernel of known "
@@ -129,6 +167,12 @@ def main():
     print("bench: generating %s inputs B=%d H=%d Nq=%d Nkv=%d D=%d" % (w.name, w.B, w.H, w.Nq, w.Nkv, w.D),
           file=sys.stderr, flush=True)
     q, k, v = make_inputs(w)
+    cpu_base = None
+    if not args.no_cpu_baseline:
+        # before the first GPU call: the oracle's worker processes then start
+        # from a parent that holds no GPU state
+        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        cpu_base = cpu_baseline(w, q, k, v, args.cpu_budget, args.cpu_workers)
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     quant = sage.sage_quant_prep(qd, kd, vd)
@@ -215,9 +259,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         res["calibration_copy_bytes"] = n
-    if not args.no_cpu_baseline:
-        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+    res["cpu_baseline"] = cpu_base
     print(json.dumps(res))
 
 
