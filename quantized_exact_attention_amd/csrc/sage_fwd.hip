@@ -63,6 +63,40 @@ __device__ __forceinline__ int masked_key_limit(int kvalid) {
   return kvalid - 4 * (lane >> 5);
 }
 
+// Scores accumulate on top of the bit pattern of 1/(2 pi), 0x3E22F983, which
+// the matrix instruction takes as an inline constant for its accumulator
+// input.  That float lies in the binade [1/8, 1/4), where consecutive floats
+// are 2^-26 apart and consecutive bit patterns are consecutive floats; its
+// pattern is 0x22F983 = 2292099 steps above the binade's start.  So for
+// -2292099 <= s < 6096509 the int32 result read as a float is exactly
+// 1/(2 pi) + s * 2^-26, and one full-rate subtraction (exact: both operands
+// in one binade) gives s * 2^-26 (v_cvt_f32_i32 issues at half the rate of
+// v_sub_f32 on gfx950).  Scaling the per-tile factor by 2^26 is exact too, so
+// fma(s * 2^-26, c * 2^26, b) rounds s * c + b exactly once, as from s itself.
+// The biased integers keep the order of the scores: the row max is taken on
+// them directly.  |s| <= 127 * 127 * D.
+constexpr int kScoreBias = 0x3E22F983;
+constexpr float kScoreUnit = 67108864.0f;   // 2^26
+static_assert(127 * 127 * 128 < 0x22F983, "biased scores must stay in one binade");
+
+// First k-step of S^T with the accumulator input set to kScoreBias.  Written
+// out because the compiler materialises a constant shared by several matrix
+// instructions in registers instead of using the inline constant.  Its result
+// is read only by the next k-step's matrix instruction of the same opcode, as
+// that instruction's accumulator input (back-to-back accumulation, which needs
+// no wait states); its inputs come from an LDS read (waited for by the
+// compiler) and from registers written once before the traversal.
+__device__ __forceinline__ v16i mfma_i8_biased(v4i a, v4i b) {
+  v16i d;
+  asm volatile("v_mfma_i32_32x32x32_i8 %0, %1, %2, 0.15915494" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// s * 2^-26 from a biased score (exact)
+__device__ __forceinline__ float score_scaled(int biased) {
+  return __int_as_float(biased) - __int_as_float(kScoreBias);
+}
+
 // log2(448): P is produced directly as 448 * 2^(s - m) = 2^(s - m + log2 448).
 constexpr float kLog2_448 = 8.80735492205760410744f;
 
@@ -85,9 +119,11 @@ __device__ __forceinline__ void issue_tile(uint8_t *dst, const int8_t *kg, const
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int c = i * 4 + wave;
-    const uint8_t *src = i < NLD / 2 ? (const uint8_t *)kg + (size_t)t * TILE + c * 1024
-                                     : vg + (size_t)t * TILE + (c - TILE / 1024) * 1024;
-    __builtin_amdgcn_global_load_lds((glb_void_t *)(src + lane * 16), (lds_void_t *)(dst + c * 1024), 16, 0, 0);
+    // fixed uniform base per chunk + one unsigned 32-bit offset (the tile and
+    // the lane) shared by the chunks: the SGPR-base addressing form
+    const uint8_t *base = i < NLD / 2 ? (const uint8_t *)kg + c * 1024 : vg + (c - TILE / 1024) * 1024;
+    const uint32_t off = (uint32_t)t * (uint32_t)TILE + (uint32_t)lane * 16u;
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(base + off), (lds_void_t *)(dst + c * 1024), 16, 0, 0);
   }
 }
 
@@ -112,14 +148,15 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   const uint8_t *kl = cur + lane * 16;        // this lane's 16 bytes of every 1 KiB operand block
   const uint8_t *vl = kl + TILE;
 
-  // ---- S^T = K_j . Q^T (int32, exact) ----
+  // ---- S^T = K_j . Q^T (int32, exact, offset by kScoreBias) ----
   v16i sacc[2];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const v4i a = *(const v4i *)(kl + (kb * NS + s) * 1024);
-      sacc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[s], s == 0 ? (v16i){} : sacc[kb], 0, 0, 0);
+      if (s == 0) sacc[kb] = mfma_i8_biased(a, qop[0]);
+      else sacc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[s], sacc[kb], 0, 0, 0);
     }
   }
   if (CAP) {
@@ -127,7 +164,7 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sc[kb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3)] = sacc[kb][v];
+      for (int v = 0; v < 16; ++v) sc[kb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3)] = sacc[kb][v] - kScoreBias;
   }
   // ragged tail: keys >= Nkv of the last tile take no part in max, sum or PV
   const int kvalid = p.Nkv - j * kBK;
@@ -155,14 +192,15 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   int mx = max(max(max(m4a, m4b), m4c), m4d);
   mx = partner_max(mx);
   const float c = (sq * load_uniform(ksc + j)) * p.sl2;   // fp32(fp32(sq * sk_j) * sl2)
-  const float mnew = __builtin_amdgcn_fmed3f(st.m, (float)mx * c, INFINITY);   // max; no NaN here
+  const float cu = c * kScoreUnit;                          // exact
+  const float mnew = __builtin_amdgcn_fmed3f(st.m, score_scaled(mx) * cu, INFINITY);   // max; no NaN here
   const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);   // "rescale"; 0 on the first tile
   const float nb = kLog2_448 - mnew;
   float pv[2][16];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) pv[kb][v] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sacc[kb][v], c, nb));
+    for (int v = 0; v < 16; ++v) pv[kb][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(score_scaled(sacc[kb][v]), cu, nb));
   if (masked) {
     const int klim = masked_key_limit(kvalid);
 #pragma unroll
@@ -295,8 +333,11 @@ __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_f
   __builtin_amdgcn_s_setprio(3);                 // finish and free the slot quickly
 
   // ---- final conversion: reciprocal of d, per-channel V scale, BF16 ----
-  const int hi = lane >> 5;
-  const int n = qb * kBQ + row;
+  // lane and row recomputed (v_mbcnt, scalar wave index) so that no register
+  // holds them through the traversal
+  const int elane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int hi = elane >> 5;
+  const int n = qb * kBQ + wave * 32 + (elane & 31);
   if (n < p.Nq) {
     const float r = 1.0f / st.dsum;               // "reciprocal" (d includes the 448)
     const int b = bh / p.H, h = bh - b * p.H;
