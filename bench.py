@@ -26,10 +26,16 @@ MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense INT8 (POP/s) and FP8 (FLOP/s) peak, 5
 
 
 def kernel_source_hash() -> str:
+    """Hash of the forward's source with comments and blank space removed, so
+    that an edit to a comment does not detach the recorded counters."""
+    import re
     h = hashlib.sha256()
     for f in ("sage_fwd.hip", "sage_common.h"):
-        with open(os.path.join(ROOT, "quantized_exact_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantized_exact_attention_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -51,7 +51,7 @@ __device__ __forceinline__ float partner_sum(float x) {
 
 // Waves per SIMD: 3 at D = 128 (at most 168 VGPRs per lane for the per-wave
 // state RO 64, S/p 32, P8 8, Q 16, partials up to 64; the kernel uses 168 with
-// no scratch), 4 at D = 64 (at most 128; it uses 97).
+// no scratch), at least 4 at D = 64 (at most 128; it uses 96, so 5 fit).
 template <int D> struct FwdOccupancy { static constexpr int waves_per_simd = D == 128 ? 3 : 4; };
 
 // Masking of the ragged last tile: lane l holds keys kb*32 + 8*(v/4) + 4*(l/32)
