@@ -51,7 +51,7 @@ __device__ __forceinline__ float partner_sum(float x) {
 
 // Waves per SIMD: 3 at D = 128 (at most 168 VGPRs per lane for the per-wave
 // state RO 64, S/p 32, P8 8, Q 16, partials up to 64; the kernel uses 168 with
-// no scratch), at least 4 at D = 64 (at most 128; it uses 96, so 5 fit).
+// no scratch), at least 4 at D = 64 (at most 128; it uses 97).
 template <int D> struct FwdOccupancy { static constexpr int waves_per_simd = D == 128 ? 3 : 4; };
 
 // Wave priority by phase of the tile (D = 64): while one wave's matrix

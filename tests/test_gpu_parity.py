@@ -391,6 +391,30 @@ def test_constant_k_and_zero_v_channel():
     stats.check()
 
 
+@pytest.mark.parametrize("D,Nq,Nkv,single_pass", [(128, 200, 1000, False), (64, 130, 258, True)])
+def test_extreme_int8_scores(D, Nq, Nkv, single_pass):
+    """Every Q and K code at +-127 with one channel sign pattern, so every score
+    is exactly +-127 * 127 * D: both ends of the int32 range the forward decodes
+    (scores accumulate on a fixed offset and are read back as floats)."""
+    g = torch.Generator().manual_seed(11)
+    sign = torch.randint(0, 2, (D,), generator=g).float() * 2 - 1
+    q = sign.expand(1, 1, Nq, D).to(torch.bfloat16).contiguous()
+    alt = torch.tensor([1.0 - 2.0 * (n % 2) for n in range(Nkv)])          # even Nkv: the K mean is 0
+    k = (alt[:, None] * sign[None, :]).reshape(1, 1, Nkv, D).to(torch.bfloat16).contiguous()
+    v = torch.randn(1, 1, Nkv, D, generator=g).to(torch.bfloat16)
+    nqb = -(-Nq // 128)
+    run = Run(q, k, v, list(range(nqb)), single_pass=single_pass)
+    p = run.oracle_prep(0)
+    assert np.all(np.abs(p.q_codes[:Nq].astype(int)) == 127) and np.all(np.abs(p.k_codes[:Nkv].astype(int)) == 127)
+    check_prep_bh(run, 0, p)
+    for ci in range(nqb):
+        nr = min(Nq, (ci + 1) * 128) - ci * 128
+        assert np.all(np.abs(run.S[ci, :nr, :Nkv].astype(np.int64)) == 127 * 127 * D)
+    stats = OStats()
+    check_units(run, stats, {0: p})
+    stats.check()
+
+
 def test_repeat_launches_bit_identical():
     """Deterministic repetition (the pages' 1,000-launch check, scaled down)."""
     w = WORKLOADS["ragged_tails"]
