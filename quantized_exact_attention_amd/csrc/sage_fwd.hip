@@ -50,20 +50,19 @@ __device__ __forceinline__ float partner_sum(float x) {
 }
 
 // Waves per SIMD: 3 at D = 128 (at most 168 VGPRs per lane for the per-wave
-// state RO 64, S/p 32, P8 8, Q 16, partials up to 64; the kernel uses 168 with
+// state RO 64, S/p 32, P8 8, Q 16, partials up to 64; the kernel uses 153 with
 // no scratch), at least 4 at D = 64 (at most 128; it uses 97).
 template <int D> struct FwdOccupancy { static constexpr int waves_per_simd = D == 128 ? 3 : 4; };
 
-// Wave priority by phase of the tile (D = 64): while one wave's matrix
-// instructions run, the SIMD's other waves issue VALU instructions at a reduced
-// rate, and the reduction is smallest for the quarter-rate exp and FP8
-// conversions (about 8 -> 11 cycles, against 2 -> 5 for an FMA).  So matrix
-// issue runs at priority 3, the exp / row-sum / pack block at 2 and the
-// full-rate scale and RO update at 1: when several waves are ready, the one
-// whose work suffers least beside matrix work issues first.  At D = 128 the
-// per-quarter stepping below is kept instead (same speed with phases, and
-// better on short traversals).
-template <int D> struct PhasePrio { static constexpr bool on = D == 64; };
+// Wave priority by phase of the tile.  While one wave's matrix instructions
+// run, the SIMD's other waves issue VALU instructions at a reduced rate, and
+// the reduction is smallest for the quarter-rate exp and FP8 conversions
+// (about 8 -> 11 cycles, against 2 -> 5 for an FMA).  So matrix issue runs at
+// priority 3, the exp / row-sum / pack block at 2, the full-rate scale
+// arithmetic before it at 1 and the RO update at 0: when several waves are
+// ready, the one whose work suffers least beside matrix work issues first,
+// and the RO update fills the gaps.
+constexpr int kPrioMatrix = 3, kPrioExp = 2, kPrioScale = 1, kPrioUpdate = 0;
 
 // Masking of the ragged last tile: lane l holds keys kb*32 + 8*(v/4) + 4*(l/32)
 // + v%4, so key (kb, v) is past Nkv iff kb*32 + 8*(v/4) + v%4 >= kvalid -
@@ -160,7 +159,7 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   const uint8_t *vl = kl + TILE;
 
   // ---- S^T = K_j . Q^T (int32, exact, offset by kScoreBias) ----
-  if (PhasePrio<D>::on) __builtin_amdgcn_s_setprio(3);
+  __builtin_amdgcn_s_setprio(kPrioMatrix);
   v16i sacc[2];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -178,7 +177,7 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
 #pragma unroll
       for (int v = 0; v < 16; ++v) sc[kb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3)] = sacc[kb][v] - kScoreBias;
   }
-  if (PhasePrio<D>::on) __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_s_setprio(kPrioScale);
   // ragged tail: keys >= Nkv of the last tile take no part in max, sum or PV
   const int kvalid = p.Nkv - j * kBK;
   const bool masked = kvalid < kBK;
@@ -209,24 +208,17 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   const float mnew = __builtin_amdgcn_fmed3f(st.m, score_scaled(mx) * cu, INFINITY);   // max; no NaN here
   const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);   // "rescale"; 0 on the first tile
   const float nb = kLog2_448 - mnew;
+  // arguments first (full rate), then the exps under the higher priority
   float pv[2][16];
-  if (PhasePrio<D>::on) {
-    // arguments first (full rate), then the exps under the higher priority
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) pv[kb][v] = __builtin_fmaf(score_scaled(sacc[kb][v]), cu, nb);
-    __builtin_amdgcn_s_setprio(2);
+    for (int v = 0; v < 16; ++v) pv[kb][v] = __builtin_fmaf(score_scaled(sacc[kb][v]), cu, nb);
+  __builtin_amdgcn_s_setprio(kPrioExp);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) pv[kb][v] = __builtin_amdgcn_exp2f(pv[kb][v]);
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) pv[kb][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(score_scaled(sacc[kb][v]), cu, nb));
-  }
+    for (int v = 0; v < 16; ++v) pv[kb][v] = __builtin_amdgcn_exp2f(pv[kb][v]);
   if (masked) {
     const int klim = masked_key_limit(kvalid);
 #pragma unroll
@@ -275,7 +267,7 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   }
 
   // ---- partial^T = V_j^T . P8^T (FP32, fresh), then RO = RO * alpha + partial ----
-  if (PhasePrio<D>::on) __builtin_amdgcn_s_setprio(3);
+  __builtin_amdgcn_s_setprio(kPrioMatrix);
   const v16f zero16 = {};
   v16f part[NS];
 #pragma unroll
@@ -285,7 +277,7 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
     const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     part[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pop, zero16, 0, 0, 0, 0, 0, 0);
   }
-  if (PhasePrio<D>::on) __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_s_setprio(kPrioUpdate);
 #pragma unroll
   for (int cb = 0; cb < NS; ++cb)
 #pragma unroll
@@ -342,20 +334,8 @@ __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_f
 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  // The SIMD issues from its oldest ready wave first, so of the workgroups that
-  // share a CU the first one runs ahead and the grid ends with CUs holding one
-  // or two workgroups.  Stepping the wave priority down each quarter of the
-  // traversal lets the workgroups that are behind catch up (D = 128; at D = 64
-  // the per-tile phase priorities above are used instead).
-  const int q1 = T / 4, q2 = T / 2, q3 = (3 * T) / 4;
-  __builtin_amdgcn_s_setprio(3);
 #pragma nounroll
   for (int j = 0; j < T; ++j) {
-    if (!PhasePrio<D>::on) {
-      if (j == q1) __builtin_amdgcn_s_setprio(2);
-      if (j == q2) __builtin_amdgcn_s_setprio(1);
-      if (j == q3) __builtin_amdgcn_s_setprio(0);
-    }
     uint8_t *cur = (j & 1) ? lds_b : lds_a;
     uint8_t *nxt = (j & 1) ? lds_a : lds_b;
     tile_step<D, CAP>(p, st, qop, sq, j, cur, nxt, kg, vg, ksc, wave, lane, row);
