@@ -53,13 +53,23 @@ def test_buffer_bytes_formulas(L):
 
 @pytest.mark.parametrize("shape,status", [
     ((1, 1, 128, 64, 96), -3), ((1, 1, 0, 64, 64), -2), ((1, 1, 64, 0, 64), -2),
-    ((0, 1, 64, 64, 64), -2), ((300, 300, 64, 64, 64), -2)])
+    ((0, 1, 64, 64, 64), -2), ((300, 300, 64, 64, 64), -2), ((1, 65536, 8, 8, 64), -2),
+    ((2, 32768, 8, 8, 64), -2), ((1, 1, (1 << 28) + 1, 64, 64), -2), ((1, 1, 64, (1 << 28) + 1, 64), -2)])
 def test_buffer_bytes_rejects_bad_shapes(L, shape, status):
     n = ctypes.c_size_t()
     s = sage.SageShape(*shape)
     assert L.sage_buffer_bytes(ctypes.byref(s), 0, ctypes.byref(n)) == status
     assert L.sage_buffer_bytes(None, 0, ctypes.byref(n)) == -1
     assert L.sage_buffer_bytes(ctypes.byref(sage.SageShape(1, 1, 8, 8, 64)), 9, ctypes.byref(n)) == -8
+
+
+@pytest.mark.parametrize("shape", [(3, 21845, 8, 8, 64), (1, 65535, 1, 1, 128), (1, 1, 1 << 28, 1 << 28, 128)])
+def test_buffer_bytes_accepts_the_limits(L, shape):
+    """B*H = 65535 (the prep's second grid dimension) and Nq = Nkv = 2^28 are accepted."""
+    n = ctypes.c_size_t()
+    assert L.sage_buffer_bytes(ctypes.byref(sage.SageShape(*shape)), 0, ctypes.byref(n)) == 0
+    B, H, Nq, _, D = shape
+    assert n.value == B * H * (-(-Nq // 128)) * 128 * D
 
 
 def _fake_quant(base=1 << 40, step=1 << 30):

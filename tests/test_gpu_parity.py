@@ -303,6 +303,25 @@ def test_single_pass_entry_falls_back_for_long_keys(Nkv, D):
     stats.check()
 
 
+def test_max_heads_sampled():
+    """B*H = 65535 (the launch limit): short ragged sequences, prep bit-exact and
+    end to end on the first, the last and six seeded heads; every output finite."""
+    B, H, Nq, Nkv, D = 3, 21845, 33, 70, 64
+    g = torch.Generator().manual_seed(17)
+    q, k, v = (torch.randn(B, H, n, D, generator=g).to(torch.bfloat16) for n in (Nq, Nkv, Nkv))
+    BH = B * H
+    heads = sample_units(1, BH, 6, 17)                        # one Q block per head: unit == head
+    run = Run(q, k, v, heads)
+    preps = {bh: run.oracle_prep(bh) for bh in heads}
+    for bh, p in preps.items():
+        check_prep_bh(run, bh, p)
+    stats = OStats()
+    check_units(run, stats, preps)
+    stats.check()
+    o = so.bf16_bits_to_f32(run.O.reshape(-1))
+    assert np.all(np.isfinite(o))
+
+
 def test_single_pass_prep_full_size_bit_identical():
     """The single pass gives the three launches' bytes on the full-size
     workloads, on 256 heads at once and at the group limit (256 groups for one
