@@ -12,6 +12,8 @@
 // (b,h); each wavefront owns 32 query rows and walks all 64-key tiles in order.
 // Per tile and wavefront:
 //   S^T[64 keys x 32 queries] = K_j . Q^T   2 x (D/32) v_mfma_i32_32x32x32_i8
+//   (accumulated on a constant offset so that each score reads back as a
+//   float with one subtraction, see kScoreBias)
 //   softmax on S^T: every lane holds ONE query and 32 of the 64 keys, so the
 //   row max / row sum are in-lane reductions plus one permlane32 swap, and
 //   m, d, alpha are per-lane scalars
@@ -21,7 +23,8 @@
 //   RO = fma(RO, alpha, partial)            (two-level accumulation)
 // K and V tiles (operand-ordered by the prep stage) are streamed through two
 // LDS buffers by global_load_lds (HBM -> LDS without registers): the copy of
-// tile j+1 is issued before tile j's math and waited for at its end.
+// tile j+1 is issued before tile j's math and waited for at its end.  Each
+// wave sets its issue priority by the phase of the tile (see kPrioMatrix).
 #include <climits>
 
 #include "sage_common.h"
