@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense INT8 (POP/s) and FP8 (FLOP/s) peak, 5.0 P
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 
 
 def kernel_source_hash() -> str:
@@ -244,6 +245,15 @@ def main():
         },
         "cpu_baseline": None,
     }
+    # The prep (three launches) is an HBM-bound stream: bytes of its two-pass
+    # schedule (bf16 Q read once and its INT8 codes written; bf16 K and V read
+    # twice and their one-byte codes written) per p50 launch time.
+    eq, ekv = w.B * w.H * w.Nq * w.D, w.B * w.H * w.Nkv * w.D
+    prep_bytes = 3 * eq + 10 * ekv
+    prep_gbs = prep_bytes / (statistics.median(prep_ms) * 1e-3) / 1e9
+    res["prep_roofline"] = {"kernels": "k_prep_pass1, k_prep_finalize, k_prep_pass2", "bound": "hbm",
+                            "achieved": prep_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": prep_gbs / HBM_PEAK_GBS, "bytes": prep_bytes}
     # SHA-256 of the forward's BF16 output bytes (deterministic across launches)
     res["output_sha256"] = hashlib.sha256(out.view(torch.int16).cpu().numpy().tobytes()).hexdigest()
     # The single-pass prep entry (K and V read once), timed apart from the step.
