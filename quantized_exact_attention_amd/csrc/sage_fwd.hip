@@ -54,8 +54,8 @@ __device__ __forceinline__ float partner_sum(float x) {
 
 // Waves per SIMD: 3 at D = 128 (at most 168 VGPRs per lane for the per-wave
 // state RO 64, S/p 32, P8 8, Q 16, partials up to 64; the kernel uses 153 with
-// no scratch), at least 4 at D = 64 (at most 128; it uses 97).
-template <int D> struct FwdOccupancy { static constexpr int waves_per_simd = D == 128 ? 3 : 4; };
+// no scratch), 5 at D = 64 (at most 96 VGPRs; no scratch in the fast build).
+template <int D> struct FwdOccupancy { static constexpr int waves_per_simd = D == 128 ? 3 : 5; };
 
 // Wave priority by phase of the tile.  While one wave's matrix instructions
 // run, the SIMD's other waves issue VALU instructions at a reduced rate, and
