@@ -7,7 +7,10 @@ unmasked entries and within one code elsewhere; BF16 output within max-abs
 of magnitude >= 2 has a bf16 spacing of 2^-6 > 1e-2, so there the bar is one
 bf16 unit in the last place of the oracle's value (any rounding difference
 before the final conversion, such as the FP8 matrix instruction's internal
-accumulation or exp2's last bit, can flip the last bf16 bit).  Small workloads are checked on every
+accumulation or exp2's last bit, can flip the last bf16 bit).  In a row where a P8 code differs from
+the oracle's (allowed above), O may in addition differ by that code's share of the row
+(p8_flip_allowance): for a key with much of the row's weight one code moves O by more than one
+bf16 unit.  Small workloads are checked on every
 row; full-size workloads on sampled 128-row units (first, last, seeded random)
 in the same launch configuration the benchmark times.
 """
@@ -126,16 +129,21 @@ class OStats:
         self.p8_total = 0
         self.p8_equal = 0
         self.p8_maxdiff = 0
+        self.flip_rows = 0
+        self.max_allowance = 0.0
 
-    def add_o(self, got_bits, ref_bits):
+    def add_o(self, got_bits, ref_bits, allowance=None):
+        """allowance: per-element extra bound for rows whose P8 codes differ
+        from the oracle's (see p8_flip_allowance); zero elsewhere."""
         g = so.bf16_bits_to_f32(got_bits).astype(np.float64)
         r = so.bf16_bits_to_f32(ref_bits).astype(np.float64)
         assert np.all(np.isfinite(g))
         d = np.abs(g - r)
+        extra = 0.0 if allowance is None else allowance
         self.max_abs = max(self.max_abs, float(d.max(initial=0)))
         self.n_o += d.size
         self.n_over += int((d > O_MAX_ABS).sum())
-        self.n_bad += int((d > np.maximum(O_MAX_ABS, bf16_ulp(r))).sum())
+        self.n_bad += int((d > np.maximum(O_MAX_ABS, bf16_ulp(r)) + extra).sum())
         self.sum_abs_diff += float(d.sum())
         self.sum_abs_ref += float(np.abs(r).sum())
 
@@ -146,15 +154,33 @@ class OStats:
 
     def check(self):
         mean_rel = self.sum_abs_diff / max(self.sum_abs_ref, 1e-300)
-        print("  O max_abs=%.3g mean_rel=%.3g (%d of %d entries above 1e-2, all within 1 bf16 ulp: %s);"
-              " P8 equal %d/%d, max code diff %d"
+        print("  O max_abs=%.3g mean_rel=%.3g (%d of %d entries above 1e-2, all within 1 bf16 ulp or a P8"
+              " flip's share: %s); P8 equal %d/%d, max code diff %d; rows with a P8 flip %d (largest"
+              " allowance %.3g)"
               % (self.max_abs, mean_rel, self.n_over, self.n_o, self.n_bad == 0, self.p8_equal,
-                 self.p8_total, self.p8_maxdiff), flush=True)
+                 self.p8_total, self.p8_maxdiff, self.flip_rows, self.max_allowance), flush=True)
         assert self.n_bad == 0, "O entries beyond max(1e-2, 1 bf16 ulp): %d" % self.n_bad
         assert mean_rel <= O_MEAN_REL
         if self.p8_total:
             assert self.p8_equal >= P8_EQUAL_FRAC * self.p8_total
             assert self.p8_maxdiff <= 1
+
+
+def p8_flip_allowance(p8_gpu, ck, p, nkv):
+    """Extra O bound for rows where the GPU's FP8 probability code differs from
+    the oracle's.  Such a difference is one code at a rounding near-tie (exp2's
+    last bit or the contracted exp2 argument), which the P8 bar allows; it moves
+    O_c by at most |dP8_k| * |V8_kc| * v_scale_c / (448 d) (later rescales only
+    shrink it), which for a key that carries much of a row's weight exceeds one
+    bf16 unit.  The bound uses the oracle's V codes, scales and final d; the GPU's
+    codes only select which keys differ.  Zero for rows without a difference."""
+    flips = p8_gpu[:, :nkv] != ck.P8[:, :nkv]
+    if not flips.any():
+        return None, 0
+    dp = np.abs(so.e4m3_decode(p8_gpu[:, :nkv]) - so.e4m3_decode(ck.P8[:, :nkv])) * flips
+    vdec = np.abs(so.e4m3_decode(p.v_codes[:nkv]).astype(np.float64))
+    extra = (dp @ vdec) * p.v_scale.astype(np.float64)[None, :] / (448.0 * ck.d[:, -1].astype(np.float64)[:, None])
+    return extra * 1.01, int(flips.any(axis=1).sum())
 
 
 def check_units(run, stats, preps):
@@ -179,7 +205,11 @@ def check_units(run, stats, preps):
         assert drel.max() <= D_RTOL, "d mismatch unit %d: max rel %.3g" % (u, drel.max())
         stats.add_p8(run.P8[ci, :nr, :run.Nkv], ck.P8[:, :run.Nkv])
         assert np.all(run.P8[ci, :nr, run.Nkv:] == 0), "masked P8 not zero"
-        stats.add_o(run.O[b, h, rows], O_ref)
+        allowance, nflip = p8_flip_allowance(run.P8[ci, :nr], ck, p, run.Nkv)
+        stats.flip_rows += nflip
+        if allowance is not None:
+            stats.max_allowance = max(stats.max_allowance, float(allowance.max()))
+        stats.add_o(run.O[b, h, rows], O_ref, allowance)
 
 
 def sample_units(nqb, BH, n_random, seed):
