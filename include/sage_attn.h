@@ -157,8 +157,12 @@ int sage_quant_prep_single_pass(const void *q, const void *k, const void *v, con
  *   P8 = E4M3FN(448 p)                            ("exact FP8 score bytes")
  *   partial = P8 . V8_j (FP8 MFMA, FP32); RO = RO * alpha + partial
  * then O = bf16(RO / d * v_scale / 448), rows < Nq stored.
- * sm_scale <= 0 selects 1/sqrt(D).  out: bf16 [B,H,Nq,D] with strides->o; it
- * must not overlap any buffer of `quant`.  One kernel launch on `stream`.
+ * sm_scale <= 0 selects 1/sqrt(D).  The exp2 argument is one FMA,
+ * fma(S, c, log2(448) - m), which rounds once where the formula above rounds
+ * twice; agreement with the formula's own FP32 evaluation to the stated
+ * tolerances holds while |m| (scaled scores, log2 units) stays below about
+ * 1500.  out: bf16 [B,H,Nq,D] with strides->o; it must not overlap any buffer
+ * of `quant`.  One kernel launch on `stream`.
  */
 int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *shape, float sm_scale, void *out,
                   const sage_strides_t *strides, void *stream);
