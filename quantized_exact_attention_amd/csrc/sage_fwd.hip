@@ -132,10 +132,13 @@ __device__ __forceinline__ void issue_tile(uint8_t *dst, const int8_t *kg, const
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int c = i * 4 + wave;
-    // fixed uniform base per chunk + one unsigned 32-bit offset (the tile and
-    // the lane) shared by the chunks: the SGPR-base addressing form
-    const uint8_t *base = i < NLD / 2 ? (const uint8_t *)kg + c * 1024 : vg + (c - TILE / 1024) * 1024;
-    const uint32_t off = (uint32_t)t * (uint32_t)TILE + (uint32_t)lane * 16u;
+    // uniform base per chunk + one unsigned 32-bit offset (the tile and the
+    // lane) shared by the chunks: the SGPR-base addressing form.  The tile
+    // index is split so that the 32-bit offset stays below 2^29 for any number
+    // of tiles; the high part moves the base once every 65536 tiles.
+    const uint8_t *base = (i < NLD / 2 ? (const uint8_t *)kg + c * 1024 : vg + (c - TILE / 1024) * 1024) +
+                          (size_t)(t >> 16) * ((size_t)TILE << 16);
+    const uint32_t off = (uint32_t)(t & 0xffff) * (uint32_t)TILE + (uint32_t)lane * 16u;
     __builtin_amdgcn_global_load_lds((glb_void_t *)(base + off), (lds_void_t *)(dst + c * 1024), 16, 0, 0);
   }
 }

@@ -58,3 +58,46 @@ def test_accuracy_against_exact_attention(name):
     print("  %s: cosine %.6f, relative L1 %.4f" % (name, cos, rl1), flush=True)
     cmin, lmax = BOUNDS[name]
     assert cos >= cmin and rl1 <= lmax
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_tiles_past_65536_against_exact_attention(D):
+    """One head with 65536 + 40 full key tiles and a ragged one (4.2M keys).
+
+    Each K/V tile is addressed as a per-chunk base plus a 32-bit offset that
+    holds the low 16 bits of the tile index; the high part moves the base.
+    This case reaches tile indices past 65536.  The keys from two tiles before
+    that index onward are shifted along a direction shared with every query, so
+    they carry over 90% of each row's softmax weight: a tile read from the
+    wrong address changes the output completely.  The oracle's prep of 4.2M
+    keys takes minutes, so the check is the method's accuracy against exact
+    attention in float64 on rows of both Q blocks (the oracle gives cosine
+    0.9991 / 0.9994 and relative L1 0.041 / 0.034 at D = 128 / 64 on the same
+    construction with 65536 cold keys).  K is rounded to multiples of 2^-12 so that its
+    column sums are exact in float64."""
+    Nq, split = 130, 65536 * 64
+    Nkv, hot0 = split + 64 * 40 + 23, split - 128
+    g = torch.Generator().manual_seed(23 + D)
+    c = (14.0 * D ** 0.5) ** 0.5                 # score shift of about 14 for the hot keys
+    u = torch.ones(D) / D ** 0.5
+    q = (torch.randn(Nq, D, generator=g) + c * u).to(torch.bfloat16)
+    k = torch.randn(Nkv, D, generator=g)
+    k[hot0:] += c * u
+    k = (torch.round(k * 4096) / 4096).to(torch.bfloat16)
+    v = torch.randn(Nkv, D, generator=g).to(torch.bfloat16)
+    print("  tiles past 65536: Nq=%d Nkv=%d D=%d" % (Nq, Nkv, D), flush=True)
+    dev = torch.device("cuda:0")
+    o = sage.sage_attention(q[None, None].to(dev), k[None, None].to(dev), v[None, None].to(dev))
+    o = o[0, 0].float().cpu().numpy().astype(np.float64)
+    rows = np.array([0, 1, 63, 64, 127, 128, 129])
+    s = k.double().numpy() @ q[rows].double().numpy().T / np.sqrt(D)      # [Nkv, rows]
+    w = np.exp(s - s.max(axis=0, keepdims=True))
+    share = w[hot0:].sum(axis=0) / w.sum(axis=0)
+    ref = (w / w.sum(axis=0, keepdims=True)).T @ v.double().numpy()
+    got = o[rows]
+    cos = float((got * ref).sum() / np.sqrt((got ** 2).sum() * (ref ** 2).sum()))
+    rl1 = float(np.abs(got - ref).sum() / np.abs(ref).sum())
+    print("  D=%d: hot share >= %.4f, cosine %.6f, relative L1 %.4f" % (D, share.min(), cos, rl1), flush=True)
+    assert share.min() > 0.9
+    assert np.all(np.isfinite(o))
+    assert cos >= 0.998 and rl1 <= 0.06
