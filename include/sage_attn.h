@@ -43,7 +43,7 @@ extern "C" {
 #define SAGE_E_SHAPE (-2)    /* B, H, Nq or Nkv out of range */
 #define SAGE_E_HEADDIM (-3)  /* D not 64 or 128 */
 #define SAGE_E_ALIGN (-4)    /* base pointer or stride misaligned */
-#define SAGE_E_ALIAS (-5)    /* the output overlaps an input or a code buffer */
+#define SAGE_E_ALIAS (-5)    /* the output overlaps itself, an input or a code buffer */
 #define SAGE_E_DEVICE (-6)   /* no device, or the device is not gfx950 */
 #define SAGE_E_LAUNCH (-7)   /* a kernel launch failed (hipGetLastError) */
 #define SAGE_E_ARG (-8)      /* another argument is invalid */
@@ -162,7 +162,10 @@ int sage_quant_prep_single_pass(const void *q, const void *k, const void *v, con
  * twice; agreement with the formula's own FP32 evaluation to the stated
  * tolerances holds while |m| (scaled scores, log2 units) stays below about
  * 1500.  out: bf16 [B,H,Nq,D] with strides->o; it must not overlap any buffer
- * of `quant`.  One kernel launch on `stream`.
+ * of `quant`, and its strides must give every element its own address
+ * (ordered by stride, each dimension of size > 1 steps past the span of the
+ * ones inside it; every packed layout qualifies), else SAGE_E_ALIAS.  One
+ * kernel launch on `stream`.
  */
 int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *shape, float sm_scale, void *out,
                   const sage_strides_t *strides, void *stream);

@@ -4,6 +4,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <utility>
 
 #include "../../include/sage_attn.h"
 #include "sage_common.h"
@@ -40,6 +41,26 @@ int check_strides(const int64_t st[3]) {
 size_t span_bytes(const sage_shape_t *s, const int64_t st[3], int N) {
   return (size_t)(((int64_t)(s->B - 1) * st[0] + (int64_t)(s->H - 1) * st[1] +
                    (int64_t)(N - 1) * st[2] + s->D) * 2);
+}
+
+// true if no two elements of a strided [B,H,N,D] tensor (d contiguous) share an
+// address: ordered by stride, every dimension of size > 1 steps past the span
+// of the dimensions inside it.  Sufficient, and it holds for every packed
+// layout and permutation of one (BHND, BNHD, ...).
+bool rows_disjoint(const sage_shape_t *s, const int64_t st[3], int N) {
+  int64_t size[3] = {s->B, s->H, N}, stride[3] = {st[0], st[1], st[2]};
+  for (int i = 1; i < 3; ++i)                    // insertion sort by stride
+    for (int j = i; j > 0 && stride[j] < stride[j - 1]; --j) {
+      std::swap(stride[j], stride[j - 1]);
+      std::swap(size[j], size[j - 1]);
+    }
+  int64_t span = s->D;
+  for (int i = 0; i < 3; ++i) {
+    if (size[i] == 1) continue;
+    if (stride[i] < span) return false;
+    span += stride[i] * (size[i] - 1);
+  }
+  return true;
 }
 
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
@@ -105,7 +126,8 @@ int fill_fwd(const sage_quant_t *q, const sage_shape_t *s, float sm_scale, void 
   if ((r = check_quant(q))) return r;
   if (!aligned16(out) || check_strides(st->o)) return SAGE_E_ALIGN;
   if (!std::isfinite(sm_scale)) return SAGE_E_ARG;
-  if (overlaps_quant(out, span_bytes(s, st->o, s->Nq), q, s)) return SAGE_E_ALIAS;
+  if (!rows_disjoint(s, st->o, s->Nq) || overlaps_quant(out, span_bytes(s, st->o, s->Nq), q, s))
+    return SAGE_E_ALIAS;
   std::memset(fp, 0, sizeof(*fp));
   fp->q_codes = q->q_codes;
   fp->q_scale = q->q_scale;
@@ -136,7 +158,7 @@ const char *sage_status_string(int status) {
     case SAGE_E_SHAPE: return "shape out of range (B, H, Nq, Nkv >= 1; B*H <= 65535)";
     case SAGE_E_HEADDIM: return "head dimension must be 64 or 128";
     case SAGE_E_ALIGN: return "base pointer not 16-byte aligned or stride not a multiple of 8 elements";
-    case SAGE_E_ALIAS: return "output overlaps an input or a quantized buffer";
+    case SAGE_E_ALIAS: return "output overlaps itself, an input or a quantized buffer";
     case SAGE_E_DEVICE: return "no HIP device, or the device is not gfx950";
     case SAGE_E_LAUNCH: return "kernel launch failed";
     case SAGE_E_ARG: return "invalid argument";

@@ -116,6 +116,17 @@ def test_fwd_validation_before_any_hip_call(L):
     assert f(ctypes.byref(qc), ctypes.byref(shape), float("nan"), out, ctypes.byref(st), None) == -8
     # output overlapping the K codes buffer
     assert f(ctypes.byref(qc), ctypes.byref(shape), 0.0, qc.k_codes + 4096, ctypes.byref(st), None) == -5
+    # output strides under which two elements share an address
+    for o in ([300 * 128, 300 * 128, 128], [2 * 300 * 128, 300 * 128, 0], [0, 300 * 128, 128],
+              [256, 128, 384], [2 * 300 * 128, 64, 256]):
+        self_overlap = _strides(2, 2, 300, 128)
+        self_overlap.o[:] = o
+        assert f(ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(self_overlap), None) == -5, o
+    # valid layouts get past the check (then fail on the missing device, not on aliasing)
+    for o in ([300 * 128 * 2, 128, 256], [256, 128, 512], [2 * 300 * 136, 300 * 136, 136]):
+        ok = _strides(2, 2, 300, 128)
+        ok.o[:] = o
+        assert f(ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(ok), None) not in (-4, -5), o
     nulls = _fake_quant()
     nulls.v_scale = None
     assert f(ctypes.byref(nulls), ctypes.byref(shape), 0.0, out, ctypes.byref(st), None) == -1
