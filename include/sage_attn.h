@@ -111,6 +111,14 @@ enum sage_buffer {
  * Returns SAGE_OK, SAGE_E_NULL, SAGE_E_SHAPE, SAGE_E_HEADDIM or SAGE_E_ARG. */
 int sage_buffer_bytes(const sage_shape_t *shape, int which, size_t *bytes);
 
+/* Byte offset inside the workspace of the single-pass prep's status word (one
+ * uint32).  sage_quant_prep_single_pass sets it to 0 before its work and to a
+ * nonzero value if one of its workgroups stopped waiting for the others of its
+ * (b,h); the outputs of that call are then invalid.  The three-launch
+ * sage_quant_prep does not use it.  Returns SAGE_OK, SAGE_E_NULL,
+ * SAGE_E_SHAPE or SAGE_E_HEADDIM. */
+int sage_prep_status_offset(const sage_shape_t *shape, size_t *offset);
+
 /*
  * Stages 1-2 of the contract ("Experiment Log", Phase 0 stage list: Q/K
  * preparation, K smoothing, INT8 quantization, FP8 V):
@@ -139,8 +147,9 @@ int sage_quant_prep(const void *q, const void *k, const void *v, const sage_shap
  * this relies on a head's workgroups all becoming resident, so do not run it
  * concurrently (other streams) with another single-pass prep or with kernels
  * that hold compute units indefinitely.  The wait is bounded (~0.1 s); one that
- * ran out leaves a nonzero status word in the workspace and the outputs of that
- * call are invalid (never observed in the tests, which check the word).  About
+ * ran out leaves a nonzero status word in the workspace (at
+ * sage_prep_status_offset) and the outputs of that call are invalid (never
+ * observed in the tests, which check the word).  About
  * as fast as sage_quant_prep on the shapes measured so far.
  */
 int sage_quant_prep_single_pass(const void *q, const void *k, const void *v, const sage_shape_t *shape,

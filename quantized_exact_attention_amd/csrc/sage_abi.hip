@@ -18,6 +18,20 @@ std::atomic<int> g_device_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// Workspace regions, each 256-byte aligned: K column partials, V column
+// partials, V inverses, then the single-pass region (arrival counters [BH],
+// ready flags [BH], the status word, then the column sums and maxima).
+size_t ws_vmax_offset(int BH, int nchunk, int D) { return align256(ws_ksum_bytes(BH, nchunk, D)); }
+size_t ws_vinv_offset(int BH, int nchunk, int D) {
+  return ws_vmax_offset(BH, nchunk, D) + align256(ws_vmax_bytes(BH, nchunk, D));
+}
+size_t ws_sync_offset(int BH, int nchunk, int D) {
+  return ws_vinv_offset(BH, nchunk, D) + align256(ws_vinv_bytes(BH, D));
+}
+size_t ws_total_bytes(int BH, int nchunk, int D) {
+  return ws_sync_offset(BH, nchunk, D) + align256(ws_sync_bytes(BH, D));
+}
+
 int check_shape(const sage_shape_t *s) {
   if (!s) return SAGE_E_NULL;
   if (s->D != 64 && s->D != 128) return SAGE_E_HEADDIM;
@@ -80,9 +94,7 @@ size_t buffer_bytes(const sage_shape_t *s, int which) {
     case SAGE_BUF_V_CODES: return BH * T * kBK * s->D;
     case SAGE_BUF_V_SCALE: return BH * s->D * sizeof(float);
     case SAGE_BUF_K_MEAN: return BH * s->D * sizeof(float);
-    case SAGE_BUF_WORKSPACE:
-      return align256(ws_ksum_bytes((int)BH, nchunk, s->D)) + align256(ws_vmax_bytes((int)BH, nchunk, s->D)) +
-             align256(ws_vinv_bytes((int)BH, s->D)) + align256(ws_sync_bytes((int)BH, s->D));
+    case SAGE_BUF_WORKSPACE: return ws_total_bytes((int)BH, nchunk, s->D);
     default: return 0;
   }
 }
@@ -187,6 +199,16 @@ int sage_buffer_bytes(const sage_shape_t *shape, int which, size_t *bytes) {
   return SAGE_OK;
 }
 
+int sage_prep_status_offset(const sage_shape_t *shape, size_t *offset) {
+  if (!offset) return SAGE_E_NULL;
+  const int r = check_shape(shape);
+  if (r) return r;
+  const int BH = shape->B * shape->H, nchunk = ceil_div(shape->Nkv, kStatChunk);
+  // single-pass region: arrival counters [BH], ready flags [BH], status word
+  *offset = ws_sync_offset(BH, nchunk, shape->D) + (size_t)2 * BH * sizeof(uint32_t);
+  return SAGE_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -234,12 +256,9 @@ int quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *
   const int BH = s->B * s->H;
   uint8_t *ws = (uint8_t *)quant->workspace;
   p.ws_ksum = (double *)ws;
-  ws += align256(ws_ksum_bytes(BH, p.nchunk, s->D));
-  p.ws_vmax = (float *)ws;
-  ws += align256(ws_vmax_bytes(BH, p.nchunk, s->D));
-  p.ws_vinv = (float *)ws;
-  ws += align256(ws_vinv_bytes(BH, s->D));
-  p.ws_sync = (uint32_t *)ws;
+  p.ws_vmax = (float *)(ws + ws_vmax_offset(BH, p.nchunk, s->D));
+  p.ws_vinv = (float *)(ws + ws_vinv_offset(BH, p.nchunk, s->D));
+  p.ws_sync = (uint32_t *)(ws + ws_sync_offset(BH, p.nchunk, s->D));
   p.ws_asum = (double *)(p.ws_sync + ws_sync_head_words(BH));
   p.ws_amax = (uint32_t *)(p.ws_asum + (size_t)BH * s->D);
   const int groups = ceil_div(s->Nkv, kFusedRows(s->D));

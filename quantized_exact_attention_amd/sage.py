@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
         L.sage_buffer_bytes.argtypes = [ctypes.POINTER(SageShape), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+        L.sage_prep_status_offset.argtypes = [ctypes.POINTER(SageShape), ctypes.POINTER(ctypes.c_size_t)]
         for name in ("sage_quant_prep", "sage_quant_prep_single_pass"):
             getattr(L, name).argtypes = [vp, vp, vp, ctypes.POINTER(SageShape), ctypes.POINTER(SageStrides),
                                          ctypes.POINTER(SageQuantC), vp]
@@ -72,8 +73,8 @@ def lib() -> ctypes.CDLL:
         L.sage_device_check.argtypes = [ctypes.c_int]
         L.sage_status_string.argtypes = [ctypes.c_int]
         L.sage_status_string.restype = ctypes.c_char_p
-        for name in ("sage_buffer_bytes", "sage_quant_prep", "sage_quant_prep_single_pass", "sage_attn_fwd",
-                     "sage_attn_fwd_capture", "sage_device_check"):
+        for name in ("sage_buffer_bytes", "sage_prep_status_offset", "sage_quant_prep",
+                     "sage_quant_prep_single_pass", "sage_attn_fwd", "sage_attn_fwd_capture", "sage_device_check"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -134,6 +135,15 @@ class SageQuant:
     @property
     def T(self) -> int:
         return -(-self.Nkv // BK)
+
+    def single_pass_status(self) -> int:
+        """Status word of the last single-pass prep into these buffers (0: every
+        wait completed; nonzero: the outputs of that call are invalid).  Reads
+        the word after synchronizing the current stream."""
+        off = ctypes.c_size_t(0)
+        _check(lib().sage_prep_status_offset(ctypes.byref(self.shape), ctypes.byref(off)), "sage_prep_status_offset")
+        torch.cuda.current_stream().synchronize()
+        return int(self.workspace[off.value:off.value + 4].cpu().view(torch.int32).item())
 
     def c_struct(self) -> SageQuantC:
         return SageQuantC(*[getattr(self, n).data_ptr() for n in BUFFERS])

@@ -16,6 +16,12 @@ int main(void) {
       const int r = sage_buffer_bytes(&shapes[i], w, &n);
       printf("buf_%d_%d %d %zu\n", i, w, r, n);
     }
+  for (int i = 0; i < 3; ++i) {
+    size_t off = 0;
+    const int r = sage_prep_status_offset(&shapes[i], &off);
+    printf("status_off_%d %d %zu\n", i, r, off);
+  }
+  printf("status_off_null %d\n", sage_prep_status_offset(&shapes[0], NULL));
   printf("sizeof_shape %zu\n", sizeof(sage_shape_t));
   printf("sizeof_strides %zu\n", sizeof(sage_strides_t));
   printf("sizeof_quant %zu\n", sizeof(sage_quant_t));

@@ -44,6 +44,21 @@ def test_buffer_sizes_match_the_binding(results):
             assert int(n) == sage.sage_buffer_bytes(*shape, w), (shape, w)
 
 
+def test_status_word_offset(results):
+    """The single pass's status word: after the K partials, the V partials and
+    the V inverses (each region 256-byte aligned), behind BH arrival counters
+    and BH ready flags, inside the workspace."""
+    a256 = lambda x: (x + 255) // 256 * 256
+    shapes = [(2, 3, 300, 700, 128), (1, 1, 1, 1, 64), (3, 21845, 33, 70, 64)]
+    for i, (B, H, Nq, Nkv, D) in enumerate(shapes):
+        status, off = (int(x) for x in results["status_off_%d" % i].split())
+        BH, nchunk = B * H, -(-Nkv // 256)
+        assert status == 0
+        assert off == a256(BH * nchunk * D * 8) + a256(BH * nchunk * D * 4) + a256(BH * D * 4) + 8 * BH
+        assert off % 4 == 0 and off + 4 <= sage.sage_buffer_bytes(B, H, Nq, Nkv, D, 7)
+    assert int(results["status_off_null"]) == -1
+
+
 def test_struct_sizes_match_the_binding(results):
     assert int(results["sizeof_shape"]) == ctypes.sizeof(sage.SageShape) == 20
     assert int(results["sizeof_strides"]) == ctypes.sizeof(sage.SageStrides) == 96

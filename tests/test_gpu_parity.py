@@ -261,7 +261,9 @@ def sync_words(run):
     a256 = lambda x: (x + 255) // 256 * 256
     off = a256(BH * nchunk * D * 8) + a256(BH * nchunk * D * 4) + a256(BH * D * 4)
     w = run.quant.workspace[off:off + 4 * (2 * BH + 1)].cpu().numpy().view(np.uint32)
-    return w[:BH], w[BH:2 * BH], int(w[2 * BH])
+    status = run.quant.single_pass_status()           # through the C ABI's offset
+    assert status == int(w[2 * BH])
+    return w[:BH], w[BH:2 * BH], status
 
 
 def fused_groups(Nkv, D):
