@@ -96,8 +96,10 @@ def sage_buffer_bytes(B: int, H: int, Nq: int, Nkv: int, D: int, which: int) -> 
     return n.value
 
 
-def _stream_handle(stream) -> ctypes.c_void_p:
-    s = torch.cuda.current_stream() if stream is None else stream
+def _stream_handle(stream, device) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    if s.device != device:
+        raise ValueError("stream is on %s, the tensors on %s" % (s.device, device))
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -136,13 +138,23 @@ class SageQuant:
     def T(self) -> int:
         return -(-self.Nkv // BK)
 
+    def check_buffers(self, device: torch.device):
+        """Every buffer on `device`, contiguous and at least as large as the C
+        ABI's size for this shape (a caller-built or reused set included)."""
+        for i, name in enumerate(BUFFERS):
+            t = getattr(self, name)
+            if not isinstance(t, torch.Tensor) or t.device != device or not t.is_contiguous():
+                raise ValueError("quant.%s must be a contiguous tensor on %s" % (name, device))
+            if t.numel() * t.element_size() < sage_buffer_bytes(self.B, self.H, self.Nq, self.Nkv, self.D, i):
+                raise ValueError("quant.%s is smaller than the shape needs" % name)
+
     def single_pass_status(self) -> int:
         """Status word of the last single-pass prep into these buffers (0: every
         wait completed; nonzero: the outputs of that call are invalid).  Reads
-        the word after synchronizing the current stream."""
+        the word after synchronizing the device."""
         off = ctypes.c_size_t(0)
         _check(lib().sage_prep_status_offset(ctypes.byref(self.shape), ctypes.byref(off)), "sage_prep_status_offset")
-        torch.cuda.current_stream().synchronize()
+        torch.cuda.synchronize(self.workspace.device)
         return int(self.workspace[off.value:off.value + 4].cpu().view(torch.int32).item())
 
     def c_struct(self) -> SageQuantC:
@@ -169,17 +181,27 @@ def sage_quant_prep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Sage
     for t in (q, k, v):
         if t.dtype != torch.bfloat16 or not t.is_cuda:
             raise TypeError("q, k, v must be bfloat16 CUDA tensors")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B,H,N,D]")
     B, H, Nq, D = q.shape
     Nkv = k.shape[2]
     if k.shape != (B, H, Nkv, D) or v.shape != (B, H, Nkv, D):
         raise ValueError("k and v must be [B,H,Nkv,D] matching q")
-    quant = out if out is not None else SageQuant.allocate(B, H, Nq, Nkv, D, q.device)
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+    if out is None:
+        quant = SageQuant.allocate(B, H, Nq, Nkv, D, q.device)
+    else:
+        if (out.B, out.H, out.Nq, out.Nkv, out.D) != (B, H, Nq, Nkv, D):
+            raise ValueError("out was allocated for another shape")
+        out.check_buffers(q.device)
+        quant = out
     st = SageStrides()
     st.q, st.k, st.v = _strides3(q), _strides3(k), _strides3(v)
     qc = quant.c_struct()
     name = "sage_quant_prep_single_pass" if single_pass else "sage_quant_prep"
     _check(getattr(lib(), name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(quant.shape),
-                                ctypes.byref(st), ctypes.byref(qc), _stream_handle(stream)), name)
+                                ctypes.byref(st), ctypes.byref(qc), _stream_handle(stream, q.device)), name)
     return quant
 
 
@@ -188,6 +210,9 @@ def _out_tensor(quant: SageQuant, out):
         out = torch.empty(quant.B, quant.H, quant.Nq, quant.D, dtype=torch.bfloat16, device=quant.q_codes.device)
     if out.dtype != torch.bfloat16 or tuple(out.shape) != (quant.B, quant.H, quant.Nq, quant.D):
         raise ValueError("out must be bfloat16 [B,H,Nq,D]")
+    if out.device != quant.q_codes.device:
+        raise ValueError("out must be on the device of the quantized buffers")
+    quant.check_buffers(out.device)
     return out
 
 
@@ -200,7 +225,7 @@ def sage_attn_fwd(quant: SageQuant, sm_scale: float | None = None, out: torch.Te
     qc = quant.c_struct()
     _check(lib().sage_attn_fwd(ctypes.byref(qc), ctypes.byref(quant.shape),
                                ctypes.c_float(0.0 if sm_scale is None else sm_scale), out.data_ptr(),
-                               ctypes.byref(st), _stream_handle(stream)), "sage_attn_fwd")
+                               ctypes.byref(st), _stream_handle(stream, out.device)), "sage_attn_fwd")
     return out
 
 
@@ -225,7 +250,7 @@ def sage_attn_fwd_capture(quant: SageQuant, units, sm_scale: float | None = None
     _check(lib().sage_attn_fwd_capture(ctypes.byref(qc), ctypes.byref(quant.shape),
                                        ctypes.c_float(0.0 if sm_scale is None else sm_scale), out.data_ptr(),
                                        ctypes.byref(st), units_t.data_ptr(), n, s_cap.data_ptr(),
-                                       p8_cap.data_ptr(), md_cap.data_ptr(), _stream_handle(stream)),
+                                       p8_cap.data_ptr(), md_cap.data_ptr(), _stream_handle(stream, dev)),
            "sage_attn_fwd_capture")
     return out, s_cap, p8_cap, md_cap
 

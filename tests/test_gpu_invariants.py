@@ -110,3 +110,26 @@ def test_graph_capture_replay_matches_eager(single_pass):
         eager = sage.sage_attention(qd, kd, vd)
         torch.cuda.synchronize()
         assert torch.equal(_bits(replayed), _bits(eager)), "replay %d differs" % r
+
+
+def test_binding_rejects_mismatched_buffers():
+    """The binding checks, before any launch, that a reused quantized set and
+    an output fit the call: same shape, same device, large enough, and an
+    output whose rows do not overlap (the C ABI's SAGE_E_ALIAS)."""
+    q, k, v = (t.to(DEV) for t in make_inputs(WORKLOADS["ragged_tails"], seed=5, B=1, H=2, Nq=130, Nkv=200, D=64))
+    quant = sage.sage_quant_prep(q, k, v)
+    with pytest.raises(ValueError, match="another shape"):
+        sage.sage_quant_prep(q[:, :, :100], k, v, out=quant)
+    small = sage.SageQuant.allocate(1, 2, 130, 200, 64, DEV)
+    small.k_codes = small.k_codes[:-64]
+    with pytest.raises(ValueError, match="smaller"):
+        sage.sage_quant_prep(q, k, v, out=small)
+    with pytest.raises(ValueError, match="device"):
+        sage.sage_attn_fwd(quant, out=torch.empty(1, 2, 130, 64, dtype=torch.bfloat16))
+    base = torch.empty(130 * 64, dtype=torch.bfloat16, device=DEV)
+    aliased = base.as_strided((1, 2, 130, 64), (0, 0, 64, 1))          # both heads on one block
+    with pytest.raises(sage.SageError, match="SAGE_E_ALIAS"):
+        sage.sage_attn_fwd(quant, out=aliased)
+    torch.cuda.synchronize()
+    ref = sage.sage_attn_fwd(quant)
+    assert torch.equal(sage.sage_attn_fwd(quant), ref)                  # the set is still usable
