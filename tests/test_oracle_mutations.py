@@ -60,6 +60,21 @@ MUTATIONS = [
      "w = np.full_like(p.v_scale, F32(1) / F32(F8MAX))"),
     ("reciprocal of the first row's d", "r = (F32(1) / dsum).astype(F32)",
      "r = np.full_like(dsum, F32(1) / dsum[0])"),
+    ("V inverse inverted", "inv = np.where(vamax == 0, F32(0), F32(F8MAX) / safe).astype(F32)",
+     "inv = np.where(vamax == 0, F32(0), safe / F32(F8MAX)).astype(F32)"),
+    ("rescale exponent sign", "alpha = exp2_f32((m - m_new).astype(F32))", "alpha = exp2_f32((m_new - m).astype(F32))"),
+    ("p against the old max", "x = (s - m_new[:, None]).astype(F32)", "x = (s - np.maximum(m, F32(-1e30))[:, None]).astype(F32)"),
+    ("output divided by the reciprocal", "o32 = ((RO * r[:, None]).astype(F32) * w[None, :]).astype(F32)",
+     "o32 = ((RO / r[:, None]).astype(F32) * w[None, :]).astype(F32)"),
+    ("K mean taken from Q", "ksum, mean = k_channel_mean(k)", "ksum, mean = k_channel_mean(q)"),
+    ("V max without abs", "vamax = np.abs(v).max(axis=0).astype(F32)", "vamax = v.max(axis=0).astype(F32)"),
+    ("q scale of the wrong block", "sq = p.q_scale[rows // BQ]", "sq = p.q_scale[np.minimum(rows // BK, p.q_scale.size - 1)]"),
+    ("tiles in reverse order", "for j in range(T):", "for j in reversed(range(T)):"),
+    ("row sum over half the tile", "ell = pr.astype(F64).sum(axis=1).astype(F32)",
+     "ell = pr[:, :32].astype(F64).sum(axis=1).astype(F32)"),
+    ("e4m3 subnormal quantum", "code = np.where(sub, np.rint(r / 2.0 ** -9), code)",
+     "code = np.where(sub, np.rint(r / 2.0 ** -10), code)"),
+    ("INT8 absmax over the whole tensor", "amax = F32(np.abs(blk).max())", "amax = F32(np.abs(x).max())"),
 ]
 
 # The pins, cheapest first (parametrized pins with one or two of their cases).
@@ -82,6 +97,7 @@ PINS = [
     ("softmax invariants", pins.test_online_softmax_invariants),
     ("equivariance", pins.test_scale_and_permutation_equivariance),
     ("cosine 128x192", lambda: pins.test_quantized_pipeline_cosine_vs_f64(128, 192, 128, 0.0, 0.999)),
+    ("per-block Q scales", pins.test_quantized_pipeline_per_q_block_scales),
     ("single tile end to end", pins.test_single_tile_workload_end_to_end),
     ("e4m3 dense sweep", pins.test_e4m3_encode_matches_torch_cast_dense_sweep),
 ]

@@ -264,6 +264,23 @@ def test_quantized_pipeline_cosine_vs_f64(nq, nkv, d, outlier, bound):
     assert cos >= bound, cos
 
 
+def test_quantized_pipeline_per_q_block_scales():
+    """Three Q blocks (the last ragged) scaled by 1, 1/8 and 4 (exact in bf16),
+    so their INT8 scales differ by those factors: each block's rows, checked on
+    their own against FP64 softmax attention, stay at the method's accuracy only
+    if every row is scored with its own block's scale."""
+    q, k, v = _tiny(300, 200, 64, 77)
+    for g, f in enumerate((1.0, 0.125, 4.0)):
+        q[g * 128:(g + 1) * 128] *= f
+    p = so.prep_bh(q, k, v)
+    assert p.q_scale[1] * 8 < p.q_scale[0] < p.q_scale[2] / 2
+    o = so.bf16_bits_to_f32(so.attention_rows(p)).astype(np.float64)
+    ref = softmax_attention_f64(q, k, v, textbook_scale(64))
+    for lo, hi in ((0, 64), (64, 128), (128, 192), (192, 256), (256, 300)):
+        a, b = o[lo:hi].ravel(), ref[lo:hi].ravel()
+        assert a @ b / np.linalg.norm(a) / np.linalg.norm(b) >= 0.995, (lo, hi)
+
+
 def test_online_softmax_invariants():
     q, k, v = _tiny(50, 400, 64, 51)
     p = so.prep_bh(q, k, v)
