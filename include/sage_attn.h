@@ -127,6 +127,13 @@ int sage_prep_status_offset(const sage_shape_t *shape, size_t *offset);
  *   Q per 128-row block, ks per 64-row block: A = max|x|, scale = fp32(A/127),
  *     code = RNE(fp32(x * fp32(127/A))) in [-127, 127]; A = 0 -> all zero
  *   V per channel: v_scale = fp32(vamax/448), code = E4M3FN_RNE(fp32(v * fp32(448/vamax)))
+ * The FP64 column sum is exact, so its order does not matter, whenever
+ * sum_t |K[t,c]| < 2^53 * u_c, u_c being the bf16 unit in the last place of the
+ * smallest nonzero |K[t,c]| of the column: for instance Nkv * (largest /
+ * smallest nonzero magnitude) below 2^45, which Gaussian-like bf16 data meets
+ * far beyond a million keys.  Outside that condition the sum rounds: this entry
+ * still gives the same bits on every call (fixed order), the single pass
+ * below may not (its partial sums meet in atomic order).
  * q, k, v: bf16 device tensors with strides->q/k/v.  Writes every buffer of
  * `quant` (including the workspace).  Launches 3 kernels on `stream`.
  */
