@@ -130,8 +130,10 @@ int sage_prep_status_offset(const sage_shape_t *shape, size_t *offset);
  * The FP64 column sum is exact, so its order does not matter, whenever
  * sum_t |K[t,c]| < 2^53 * u_c, u_c being the bf16 unit in the last place of the
  * smallest nonzero |K[t,c]| of the column: for instance Nkv * (largest /
- * smallest nonzero magnitude) below 2^45, which Gaussian-like bf16 data meets
- * far beyond a million keys.  Outside that condition the sum rounds: this entry
+ * smallest nonzero magnitude) below 2^45.  Gaussian-like bf16 data meets it up
+ * to about a million keys (its smallest magnitude shrinks like 1/Nkv); data on
+ * a coarser grid (multiples of 2^-12, say) much further.  Outside that
+ * condition the sum rounds: this entry
  * still gives the same bits on every call (fixed order), the single pass
  * below may not (its partial sums meet in atomic order).
  * q, k, v: bf16 device tensors with strides->q/k/v.  Writes every buffer of
