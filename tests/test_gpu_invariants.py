@@ -133,3 +133,21 @@ def test_binding_rejects_mismatched_buffers():
     torch.cuda.synchronize()
     ref = sage.sage_attn_fwd(quant)
     assert torch.equal(sage.sage_attn_fwd(quant), ref)                  # the set is still usable
+
+
+@pytest.mark.parametrize("single_pass", [False, True])
+def test_calls_with_preallocated_buffers_allocate_nothing(single_pass):
+    """With the quantized set and the output passed in, prep + forward make no
+    device allocation (torch's allocator counts every request, cached or not):
+    the path a captured graph or an allocation-free caller relies on."""
+    q, k, v = (t.to(DEV) for t in make_inputs(WORKLOADS["ragged_tails"], seed=8, B=1, H=3, Nq=200, Nkv=300, D=128))
+    quant = sage.sage_quant_prep(q, k, v, single_pass=single_pass)
+    out = sage.sage_attn_fwd(quant)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_stats(DEV)["allocation.all.allocated"]
+    for _ in range(3):
+        sage.sage_quant_prep(q, k, v, out=quant, single_pass=single_pass)
+        sage.sage_attn_fwd(quant, out=out)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_stats(DEV)["allocation.all.allocated"] == before
+    assert torch.equal(_bits(out), _bits(sage.sage_attention(q, k, v)))
