@@ -53,7 +53,7 @@ __device__ __forceinline__ float partner_sum(float x) {
 }
 
 // Waves per SIMD: 3 at D = 128 (at most 168 VGPRs per lane for the per-wave
-// state RO 64, S/p 32, P8 8, Q 16, partials up to 64; the kernel uses 153 with
+// state RO 64, S/p 32, P8 8, Q 16, partials up to 64; the kernel uses 152 with
 // no scratch), 5 at D = 64 (at most 96 VGPRs; no scratch in the fast build).
 template <int D> struct FwdOccupancy { static constexpr int waves_per_simd = D == 128 ? 3 : 5; };
 
