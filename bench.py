@@ -270,6 +270,20 @@ def main():
             sp_ms.append((a, b))
     torch.cuda.synchronize()
     res["prep_single_pass_ms_p50"] = statistics.median(a.elapsed_time(b) for a, b in sp_ms)
+    if w.name == "single_tile":
+        # the pages quote this fixture's forward both batched and as single
+        # launches (2,000 samples); time single launches the same way: one
+        # forward, then a full synchronization, per sample
+        single = []
+        for _ in range(2000):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            sage.sage_attn_fwd(quant, out=out)
+            b.record(stream)
+            torch.cuda.synchronize()
+            single.append(a.elapsed_time(b))
+        res["fwd_single_launch"] = {"samples": len(single), "p50_ms": statistics.median(single),
+                                    "cv": statistics.pstdev(single) / statistics.mean(single)}
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
