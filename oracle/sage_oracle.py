@@ -154,9 +154,39 @@ def fma_f32(a: np.ndarray, b: np.ndarray, c: np.ndarray) -> np.ndarray:
 
 
 def exp2_f32(x: np.ndarray) -> np.ndarray:
-    """fp32(2^x) for float32 x, evaluated in float64 and rounded once."""
-    with np.errstate(over="ignore", under="ignore"):
-        return np.exp2(np.asarray(x, F32).astype(F64)).astype(F32)
+    """Correctly rounded fp32(2^x) for float32 x.
+
+    2^x is evaluated in float64 (error below one float64 unit) and rounded to
+    float32.  That rounding can only go the wrong way where the float64 value
+    lies within a few float64 units of a midpoint between adjacent float32
+    values (about one float32 argument in ten million); every value within
+    2^-20 float32 units of a midpoint is evaluated again with 50-digit
+    arithmetic (mpmath) and rounded from that, ties (only 2^-150, halfway
+    between 0 and the smallest subnormal) to even.
+    """
+    xf = np.asarray(x, F32)
+    shape = xf.shape
+    xf = xf.reshape(-1)
+    with np.errstate(all="ignore"):
+        y = np.exp2(xf.astype(F64))
+        r = y.astype(F32)
+        rf = r.astype(F64)
+        lo = np.where(rf > y, np.nextafter(r, F32(-np.inf)), r).astype(F64)
+        hi = np.nextafter(lo.astype(F32), F32(np.inf)).astype(F64)
+        near = np.abs(y - (lo + hi) / 2.0) < (hi - lo) * 2.0 ** -20
+    if np.any(near):
+        import mpmath
+        r = np.array(r, dtype=F32, copy=True)
+        with mpmath.workdps(50):
+            for i in np.nonzero(near)[0]:
+                exact = mpmath.power(2, mpmath.mpf(float(xf[i])))
+                below, above = exact - mpmath.mpf(float(lo[i])), mpmath.mpf(float(hi[i])) - exact
+                if below == above:      # an exact tie (2^-150): to the even neighbour
+                    take_lo = (int(F32(lo[i]).view(np.uint32)) & 1) == 0
+                else:
+                    take_lo = below < above
+                r[i] = F32(lo[i]) if take_lo else F32(hi[i])
+    return r.reshape(shape)
 
 
 # ---------------------------------------------------------------------------

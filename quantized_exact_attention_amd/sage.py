@@ -11,7 +11,6 @@ Names mirror the C ABI in ``include/sage_attn.h``.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 
@@ -258,7 +257,3 @@ def sage_attn_fwd_capture(quant: SageQuant, units, sm_scale: float | None = None
 def sage_attention(q, k, v, sm_scale: float | None = None) -> torch.Tensor:
     """Both calls of the hot path: prep then fused forward."""
     return sage_attn_fwd(sage_quant_prep(q, k, v), sm_scale)
-
-
-def default_sm_scale(D: int) -> float:
-    return 1.0 / math.sqrt(D)

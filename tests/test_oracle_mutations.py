@@ -75,6 +75,30 @@ MUTATIONS = [
     ("e4m3 subnormal quantum", "code = np.where(sub, np.rint(r / 2.0 ** -9), code)",
      "code = np.where(sub, np.rint(r / 2.0 ** -10), code)"),
     ("INT8 absmax over the whole tensor", "amax = F32(np.abs(blk).max())", "amax = F32(np.abs(x).max())"),
+    # rounding points of the readings
+    ("INT8 ties away from zero", "q = np.rint((blk * inv).astype(F32))",
+     "q = np.sign(blk) * np.floor(np.abs((blk * inv).astype(F32)) + F32(0.5))"),
+    ("INT8 code by per-element division", "q = np.rint((blk * inv).astype(F32))",
+     "q = np.rint((blk / scales[g]).astype(F32))"),
+    ("V code by per-element division", "codes[:n] = e4m3_encode((v * inv[None, :]).astype(F32))",
+     "codes[:n] = e4m3_encode((v / np.where(vscale == 0, F32(1), vscale)[None, :]).astype(F32))"),
+    ("exp2 evaluated in float32", "y = np.exp2(xf.astype(F64))", "y = np.exp2(xf).astype(F64)"),
+    ("exp2 without the near-midpoint refinement", "if np.any(near):", "if False:"),
+    ("row sum in float32", "ell = pr.astype(F64).sum(axis=1).astype(F32)", "ell = pr.sum(axis=1, dtype=F32)"),
+    ("score factor rounded once", "cj = F32(F32(sq * p.k_scale[j]) * sl2)",
+     "cj = (sq.astype(F64) * F64(p.k_scale[j]) * F64(sl2)).astype(F32)"),
+    ("exp2 argument rounded once", "x = (s - m_new[:, None]).astype(F32)",
+     "x = (S.astype(F64) * cj[:, None].astype(F64) - m_new[:, None].astype(F64)).astype(F32)"),
+    ("output scaled in one rounding", "o32 = ((RO * r[:, None]).astype(F32) * w[None, :]).astype(F32)",
+     "o32 = (RO.astype(F64) * r[:, None].astype(F64) * w[None, :].astype(F64)).astype(F32)"),
+    ("output scale folded before the reciprocal", "o32 = ((RO * r[:, None]).astype(F32) * w[None, :]).astype(F32)",
+     "o32 = (RO * (r[:, None] * w[None, :]).astype(F32)).astype(F32)"),
+    ("partial added before the rescale", "RO = fma_f32(RO, alpha[:, None], partial)",
+     "RO = ((RO + partial) * alpha[:, None]).astype(F32)"),
+    ("K mean divided in float32", "mean = (ksum / F64(k.shape[0])).astype(F32)",
+     "mean = (ksum.astype(F32) / F32(k.shape[0])).astype(F32)"),
+    ("1/448 folded into the reciprocal", "r = (F32(1) / dsum).astype(F32)",
+     "r = (F32(1) / (dsum * F32(F8MAX))).astype(F32); w = p.v_scale"),
 ]
 
 # The pins, cheapest first (parametrized pins with one or two of their cases).
@@ -85,6 +109,7 @@ PINS = [
     ("bf16 rne", pins.test_bf16_rne_matches_torch_cast),
     ("fma exact", pins.test_fma_f32_exact_rational),
     ("k mean exact", pins.test_k_mean_exact_rational),
+    ("k mean exact, wide exponents", pins.test_k_mean_exact_rational_wide_exponents),
     ("int8 invariants", pins.test_int8_block_quant_bounds_and_invariants),
     ("v fp8", pins.test_v_fp8_channel_quant),
     ("scores 5x7", lambda: pins.test_scores_brute_force_int(5, 7, 64)),
@@ -100,6 +125,13 @@ PINS = [
     ("per-block Q scales", pins.test_quantized_pipeline_per_q_block_scales),
     ("single tile end to end", pins.test_single_tile_workload_end_to_end),
     ("e4m3 dense sweep", pins.test_e4m3_encode_matches_torch_cast_dense_sweep),
+    ("int8 ties", pins.test_int8_ties_round_half_to_even),
+    ("int8 reciprocal rule", pins.test_int8_code_multiplies_by_rounded_reciprocal),
+    ("v reciprocal rule", pins.test_v_code_multiplies_by_rounded_reciprocal),
+    ("exp2 vs mpmath", pins.test_exp2_f32_correctly_rounded_against_mpmath),
+    ("tile 0 exact, full", lambda: pins.test_tile0_softmax_exact_rounding_points(64)),
+    ("tile 0 exact, ragged", lambda: pins.test_tile0_softmax_exact_rounding_points(41)),
+    ("final conversion exact", pins.test_final_conversion_rounding_points),
 ]
 
 

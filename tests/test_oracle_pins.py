@@ -6,7 +6,12 @@ exact rational arithmetic (fractions) for the K mean and for fma; brute-force
 integer dot products for the scores; closed forms (two-pass softmax attention
 in float64, online == two-pass when quantization is off); invariants (K
 smoothing leaves softmax unchanged, scale equivariance, permutation
-equivariance); special cases with known answers (one key, constant K).
+equivariance); special cases with known answers (one key, constant K); and
+every rounding point of the readings recomputed exactly (fractions, mpmath's
+2^x at 50 digits): INT8 ties, the multiply-by-rounded-reciprocal rules of the
+INT8 and V codes, exp2 over a dense sweep and its hardest arguments, the
+first tile's scores, running max, row sum and P8 codes, and the final
+conversion.
 """
 
 import math
@@ -145,6 +150,18 @@ def test_k_mean_exact_rational():
         assert Fraction(float(ksum[c])) == exact
         # float64 quotient rounded to float32 equals the correctly rounded mean here
         assert mean[c] == _round_fraction_to_f32(exact / 37)
+
+
+def test_k_mean_exact_rational_wide_exponents():
+    """Column sums with more significant bits than float32 holds (entries from
+    2^-24 to 2^4): the mean is the exact sum divided by Nkv, rounded once."""
+    rng = np.random.default_rng(13)
+    k = bf16_exact((53, 300), rng) * np.exp2(rng.integers(-24, 4, (53, 300))).astype(np.float32)
+    ksum, mean = so.k_channel_mean(k)
+    for c in range(300):
+        exact = sum(Fraction(float(x)) for x in k[:, c])
+        assert Fraction(float(ksum[c])) == exact
+        assert mean[c] == _round_fraction_to_f32(exact / 53), c
 
 
 def test_int8_block_quant_bounds_and_invariants():
@@ -371,3 +388,243 @@ def test_single_tile_workload_end_to_end():
     o = so.bf16_bits_to_f32(O).astype(np.float64)
     cos = (o.ravel() @ ref.ravel()) / np.linalg.norm(o) / np.linalg.norm(ref)
     assert cos >= 0.999
+
+
+# ------------------------------------------- rounding points, pinned exactly --
+# The readings fix the rounding of every step; the pins below compute each
+# expected value with exact rational arithmetic (fractions) or 50-digit
+# arithmetic (mpmath) and round it once by hand, independently of numpy's
+# float32 arithmetic and of the oracle's own helpers.
+
+def _rne_int(fr: Fraction) -> int:
+    """Nearest integer to a rational, ties to even."""
+    fl = math.floor(fr)
+    rem = fr - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        return fl + 1
+    return fl
+
+
+def test_int8_ties_round_half_to_even():
+    """Block absmax 127, so fp32(127/A) = 1 exactly and every code is x itself
+    rounded: halves go to the even neighbour (0.5 -> 0, 1.5 -> 2, 2.5 -> 2,
+    126.5 -> 126)."""
+    vals = [127.0, 0.5, -0.5, 1.5, -1.5, 2.5, -2.5, 126.5, -126.5, 3.5, -3.5, 0.0]
+    x = np.zeros((64, 16), np.float32)
+    x[:len(vals), 0] = vals
+    assert np.array_equal(f32(vals), torch.tensor(vals).to(torch.bfloat16).float().numpy())
+    codes, scales = so.quantize_int8_blocks(x, 64)
+    assert scales[0] == np.float32(1.0)
+    want = [127, 0, 0, 2, -2, 2, -2, 126, -126, 4, -4, 0]
+    assert [int(c) for c in codes[:len(vals), 0]] == want
+
+
+def _bf16_grid(lo, hi):
+    """Every positive bfloat16 value in [lo, hi), as float32."""
+    a = int(np.float32(lo).view(np.uint32)) >> 16
+    b = int(np.float32(hi).view(np.uint32)) >> 16
+    return (np.arange(a, b, dtype=np.uint32) << 16).view(np.float32)
+
+
+def _int8_cases():
+    """(A, x) pairs of bf16 values where the literal rule RNE(fp32(x * fp32(127/A)))
+    and the per-element division RNE(fp32(x / fp32(A/127))) give different codes
+    (found with numpy float32 arithmetic; the expected codes are recomputed
+    exactly below)."""
+    out = []
+    for A in _bf16_grid(1.0, 8.0)[::7]:
+        inv = np.float32(127) / A
+        sc = A / np.float32(127)
+        xs = _bf16_grid(0.01, float(A))
+        lit = np.rint((xs * inv).astype(np.float32))
+        div = np.rint((xs / sc).astype(np.float32))
+        for xv in xs[lit != div][:2]:
+            out.append((float(A), float(xv)))
+        if len(out) >= 12:
+            break
+    return out
+
+
+def test_int8_code_multiplies_by_rounded_reciprocal():
+    """Reading of the INT8 rule: code = RNE(fp32(x * fp32(127/A))), one
+    correctly rounded reciprocal per block, not a division per element."""
+    cases = _int8_cases()
+    assert len(cases) >= 4
+    n_div_differs = 0
+    for A, xv in cases:
+        blk = np.zeros((64, 4), np.float32)
+        blk[0, 0], blk[1, 1], blk[2, 2] = A, xv, -xv
+        codes, scales = so.quantize_int8_blocks(blk, 64)
+        inv = _round_fraction_to_f32(Fraction(127) / Fraction(A))
+        prod = _round_fraction_to_f32(Fraction(xv) * Fraction(float(inv)))
+        want = _rne_int(Fraction(float(prod)))
+        assert int(codes[1, 1]) == want and int(codes[2, 2]) == -want, (A, xv)
+        assert scales[0] == _round_fraction_to_f32(Fraction(A) / 127)
+        sc = _round_fraction_to_f32(Fraction(A) / 127)
+        alt = _rne_int(Fraction(float(_round_fraction_to_f32(Fraction(xv) / Fraction(float(sc))))))
+        n_div_differs += alt != want
+    assert n_div_differs == len(cases)
+
+
+def _v_cases():
+    """(vamax, v) bf16 pairs where E4M3(fp32(v * fp32(448/vamax))) and
+    E4M3(fp32(v / fp32(vamax/448))) differ (found with numpy float32 and torch's
+    E4M3 cast)."""
+    out = []
+    for amax in _bf16_grid(0.5, 16.0)[::5]:
+        inv = np.float32(448) / amax
+        sc = amax / np.float32(448)
+        vs = _bf16_grid(0.001, float(amax))
+        a = torch.from_numpy((vs * inv).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        b = torch.from_numpy((vs / sc).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        for v in vs[a != b][:2]:
+            out.append((float(amax), float(v)))
+        if len(out) >= 12:
+            break
+    return out
+
+
+def test_v_code_multiplies_by_rounded_reciprocal():
+    """Reading of the V rule: code = E4M3_RNE(fp32(v * fp32(448/vamax))); the
+    E4M3 rounding of the exactly rounded product is torch's cast."""
+    cases = _v_cases()
+    assert len(cases) >= 4
+    for amax, v in cases:
+        col = np.zeros((3, 1), np.float32)
+        col[0, 0], col[1, 0], col[2, 0] = amax, v, -v
+        codes, vs, _ = so.quantize_v_channels(col, 64)
+        inv = _round_fraction_to_f32(Fraction(448) / Fraction(amax))
+        prod = _round_fraction_to_f32(Fraction(v) * Fraction(float(inv)))
+        want = torch.tensor([float(prod), -float(prod)], dtype=torch.float32).to(torch.float8_e4m3fn)
+        assert [int(c) for c in codes[1:3, 0]] == want.view(torch.uint8).tolist(), (amax, v)
+        assert vs[0] == _round_fraction_to_f32(Fraction(amax) / 448)
+        sc = _round_fraction_to_f32(Fraction(amax) / 448)
+        alt = _round_fraction_to_f32(Fraction(v) / Fraction(float(sc)))
+        assert torch.tensor([float(alt)]).to(torch.float8_e4m3fn).view(torch.uint8).item() != int(codes[1, 0])
+
+
+def _exp2_correct_f32(x) -> np.float32:
+    """2^x at 50 digits, rounded to the nearer float32 neighbour."""
+    import mpmath
+    with mpmath.workdps(50):
+        e = mpmath.power(2, mpmath.mpf(float(x)))
+        c = np.float32(float(e))
+        best = None
+        for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+            key = (abs(mpmath.mpf(float(cand)) - e), int(np.float32(cand).view(np.uint32)) & 1)  # ties: even
+            if best is None or key < best[0]:
+                best = (key, cand)
+    return np.float32(best[1])
+
+
+def _exp2_hard_arguments():
+    """float32 arguments whose 2^x lies closest to a float32 rounding midpoint
+    (tests/golden/exp2_near_midpoint_args.txt, bit patterns; from an exhaustive
+    scan of [-150, 0])."""
+    with open(os.path.join(GOLDEN, "exp2_near_midpoint_args.txt")) as fh:
+        bits = [int(l.split()[0], 16) for l in fh if l.strip() and not l.startswith("#")]
+    return np.array(bits, dtype=np.uint32).view(np.float32)
+
+
+def test_exp2_f32_correctly_rounded_against_mpmath():
+    """p = fp32(2^x) correctly rounded (reading of the softmax step): a dense
+    sweep of [-150, 0], random arguments and the hardest cases near midpoints."""
+    rng = np.random.default_rng(9)
+    x = np.concatenate([np.linspace(-150, 0, 6001, dtype=np.float32),
+                        rng.uniform(-40, 0, 3000).astype(np.float32),
+                        -np.exp2(rng.uniform(-30, 2, 1000)).astype(np.float32),
+                        _exp2_hard_arguments()])
+    got = so.exp2_f32(x)
+    want = np.array([_exp2_correct_f32(v) for v in x], dtype=np.float32)
+    bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, [(float(x[i]), float(got[i]), float(want[i])) for i in bad[:5]]
+    assert so.exp2_f32(np.float32(-np.inf)) == 0 and so.exp2_f32(np.float32(0)) == 1
+
+
+def _tile0_exact(p, rows, sm):
+    """Tile 0 of the traversal recomputed with exact arithmetic: s, m, p, l and
+    P8 for the given rows (a single-tile head, so d after tile 0 is l)."""
+    import mpmath
+    with mpmath.workdps(50):
+        log2e = _round_fraction_to_f32(Fraction(mpmath.nstr(1 / mpmath.log(2), 45)))
+    sl2 = _round_fraction_to_f32(Fraction(float(sm)) * Fraction(float(log2e)))
+    nreal = min(64, p.nkv)
+    out = []
+    for i in rows:
+        sq = p.q_scale[i // 128]
+        c = _round_fraction_to_f32(Fraction(float(_round_fraction_to_f32(Fraction(float(sq)) * Fraction(float(p.k_scale[0]))))) * Fraction(float(sl2)))
+        S = [sum(int(p.q_codes[i, ch]) * int(p.k_codes[t, ch]) for ch in range(p.d)) for t in range(nreal)]
+        s = [_round_fraction_to_f32(Fraction(St) * Fraction(float(c))) for St in S]
+        m = max(s)
+        x = [_round_fraction_to_f32(Fraction(float(si)) - Fraction(float(m))) for si in s]
+        pr = [_exp2_correct_f32(xi) for xi in x]
+        ell = _round_fraction_to_f32(sum(Fraction(float(v)) for v in pr))
+        p448 = [_round_fraction_to_f32(Fraction(float(v)) * 448) for v in pr]
+        p8 = torch.tensor([float(v) for v in p448], dtype=torch.float32).to(torch.float8_e4m3fn)
+        out.append((m, ell, p8.view(torch.uint8).numpy()))
+    return out
+
+
+@pytest.mark.parametrize("nkv", [64, 41])
+def test_tile0_softmax_exact_rounding_points(nkv):
+    """One 64-key tile (full, or ragged with masked keys): m, d = l (the row sum
+    of the unquantized p, correctly rounded once) and the P8 codes against exact
+    rational arithmetic and mpmath's 2^x, on 128 rows."""
+    q, k, v = _tiny(128, nkv, 64, 300 + nkv, outlier=0.02)
+    p = so.prep_bh(q, k, v)
+    rows = np.arange(128)
+    _, ck = so.attention_rows(p, rows, want_checkpoints=True)
+    exact = _tile0_exact(p, rows, np.float32(0.125))          # 1/sqrt(64)
+    for i, (m, ell, p8) in enumerate(exact):
+        assert ck.m[i, 0] == m, i
+        assert ck.alpha[i, 0] == 0
+        assert ck.d[i, 0] == ell, (i, float(ck.d[i, 0]), float(ell))
+        assert np.array_equal(ck.P8[i, :nkv], p8), i
+        assert np.all(ck.P8[i, nkv:64] == 0)
+
+
+def _final_order_alternatives(RO, r, vs):
+    """bf16 bits of the output under the contract's rounding order and under
+    three reorderings (numpy float32 arithmetic; used only to choose inputs)."""
+    F32 = np.float32
+    w = (vs / F32(448)).astype(F32)
+    as_bf16 = lambda a: torch.from_numpy(np.asarray(a, F32)).to(torch.bfloat16).view(torch.int16).numpy()
+    ref = as_bf16(((RO * r).astype(F32) * w).astype(F32))
+    alts = [as_bf16((RO.astype(np.float64) * np.float64(r) * w.astype(np.float64)).astype(F32)),
+            as_bf16((RO * (r * w).astype(F32)).astype(F32)),
+            as_bf16(((RO * (F32(1) / (F32(1) / r * F32(448))).astype(F32)).astype(F32) * vs).astype(F32))]
+    return ref, alts
+
+
+def test_final_conversion_rounding_points():
+    """Constant K: every real key scores 0, so p = 1, d = n, P8 = 448 and
+    RO = fp32(448 * sum_t dec(V8[t, c])) (the exact tile sum rounded once).  The
+    output must be bf16(fp32(fp32(RO * fp32(1/d)) * fp32(v_scale/448))), checked
+    with exact rationals on a wide head whose seed is chosen (numpy search) so
+    that three reorderings of the final scaling change some bf16 outputs."""
+    n, D = 3, 4096
+    for seed in range(200):
+        rng = np.random.default_rng(1000 + seed)
+        v = bf16_exact((n, D), rng)
+        codes, vs, _ = so.quantize_v_channels(v, 64)   # choosing the inputs only
+        RO = (448.0 * so.e4m3_decode(codes[:n]).sum(axis=0)).astype(np.float32)
+        ref, alts = _final_order_alternatives(RO, np.float32(1) / np.float32(n), vs)
+        if all((a != ref).any() for a in alts):
+            break
+    else:
+        pytest.fail("no discriminating input found")
+    k = np.repeat(bf16_exact((1, D), rng), n, axis=0)
+    q = bf16_exact((2, D), rng)
+    p = so.prep_bh(q, k, v)
+    assert np.all(p.k_codes == 0)
+    O, ck = so.attention_rows(p, want_checkpoints=True)
+    r = _round_fraction_to_f32(Fraction(1, n))
+    want = np.zeros(D, np.float32)
+    for c in range(D):
+        ro = _round_fraction_to_f32(sum(Fraction(448) * Fraction(float(x)) for x in so.e4m3_decode(p.v_codes[:n, c])))
+        assert ck.RO[0, c] == ro
+        w = _round_fraction_to_f32(Fraction(float(p.v_scale[c])) / 448)
+        want[c] = _round_fraction_to_f32(Fraction(float(_round_fraction_to_f32(Fraction(float(ro)) * Fraction(float(r))))) * Fraction(float(w)))
+    assert ck.r[0] == r
+    want_bits = torch.from_numpy(want).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O[0], want_bits) and np.array_equal(O[1], want_bits)
