@@ -191,19 +191,25 @@ int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *shape, float sm
 /*
  * Diagnostic variant of sage_attn_fwd (same kernel source, capture build):
  * runs only the n_units work units listed in `units` (device int32 array;
- * unit = ((b*H + h) * NQB + qblock)) and, besides their O rows, writes the
- * checkpoints of the Phase 2B prototype description for them:
- *   s_cap   int32 [n_units][128][T*64]   QK scores (pad keys: the raw score)
- *   p8_cap  uint8 [n_units][128][T*64]   FP8 probability codes (masked: 0)
- *   md_cap  float [n_units][128][T][2]   running max m and 448*d after tile j
- * Rows >= Nq of a unit hold values for zero pad codes.  Unit ids must be
- * distinct; the kernel skips ids outside [0, B*H*NQB) and their capture slots
- * are left unwritten.
+ * unit = ((b*H + h) * NQB + qblock)) and, besides their O rows, writes all
+ * nine checkpoints of the Phase 2B prototype description (QK, m, d, FP8
+ * probability, rescale, PV partial, FP32 RO, reciprocal, BF16 output) for them:
+ *   s_cap    int32 [n_units][128][T*64]  QK scores (pad keys: the raw score)
+ *   p8_cap   uint8 [n_units][128][T*64]  FP8 probability codes (masked: 0)
+ *   md_cap   float [n_units][128][T][3]  after tile j: running max m, 448*d and
+ *                                        the rescale factor alpha of tile j
+ *   part_cap float [n_units][128][T][D]  PV partial of tile j (P8 . V8_j, FP32)
+ *   ro_cap   float [n_units][128][T][D]  RO after tile j
+ *   r_cap    float [n_units][128]        reciprocal 1/(448*d) of the final d
+ * (P is carried as 448 * p, so d carries the factor 448 too.)  Rows >= Nq of a
+ * unit hold values for zero pad codes.  Unit ids must be distinct; the kernel
+ * skips ids outside [0, B*H*NQB) and their capture slots are left unwritten.
+ * Every capture pointer must be 16-byte aligned.
  */
 int sage_attn_fwd_capture(const sage_quant_t *quant, const sage_shape_t *shape, float sm_scale,
                           void *out, const sage_strides_t *strides, const int32_t *units,
                           int32_t n_units, int32_t *s_cap, uint8_t *p8_cap, float *md_cap,
-                          void *stream);
+                          float *part_cap, float *ro_cap, float *r_cap, void *stream);
 
 /* SAGE_OK if `device` is a gfx950 GPU, else SAGE_E_DEVICE (one HIP query). */
 int sage_device_check(int device);

@@ -316,6 +316,8 @@ class Checkpoints:
     RO: np.ndarray       # float32 [R, D]   running output after the last tile
     r: np.ndarray        # float32 [R]      reciprocal of d
     O: np.ndarray        # uint16 [R, D]    bf16 output bits
+    partial: np.ndarray  # float32 [R, T, D] PV partial of tile j
+    RO_tiles: np.ndarray  # float32 [R, T, D] running output after tile j
 
 
 def default_sm_scale(d: int) -> np.float32:
@@ -362,6 +364,8 @@ def attention_rows(p: PrepBH, rows: np.ndarray | None = None, sm_scale: float | 
         m_all = np.zeros((R, T), dtype=F32)
         d_all = np.zeros((R, T), dtype=F32)
         a_all = np.zeros((R, T), dtype=F32)
+        part_all = np.zeros((R, T, D), dtype=F32)
+        ro_all = np.zeros((R, T, D), dtype=F32)
 
     vdec_all = e4m3_decode(p.v_codes)                    # float64 [Tpad, D]
     for j in range(T):
@@ -417,13 +421,15 @@ def attention_rows(p: PrepBH, rows: np.ndarray | None = None, sm_scale: float | 
             m_all[:, j] = m
             d_all[:, j] = dsum
             a_all[:, j] = alpha
+            part_all[:, j] = partial
+            ro_all[:, j] = RO
     # final conversion: reciprocal, per-channel V scale folded with 1/448, bf16
     r = (F32(1) / dsum).astype(F32)
     w = (p.v_scale / F32(F8MAX)).astype(F32)
     o32 = ((RO * r[:, None]).astype(F32) * w[None, :]).astype(F32)
     O = bf16_bits_rne(o32)
     if want_checkpoints:
-        return O, Checkpoints(S_all, P8_all, m_all, d_all, a_all, RO, r, O)
+        return O, Checkpoints(S_all, P8_all, m_all, d_all, a_all, RO, r, O, part_all, ro_all)
     return O
 
 

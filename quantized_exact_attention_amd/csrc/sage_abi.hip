@@ -292,18 +292,24 @@ int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *s, float sm_sca
 
 int sage_attn_fwd_capture(const sage_quant_t *quant, const sage_shape_t *s, float sm_scale, void *out,
                           const sage_strides_t *st, const int32_t *units, int32_t n_units, int32_t *s_cap,
-                          uint8_t *p8_cap, float *md_cap, void *stream) {
+                          uint8_t *p8_cap, float *md_cap, float *part_cap, float *ro_cap, float *r_cap,
+                          void *stream) {
   FwdParams fp;
   int r = fill_fwd(quant, s, sm_scale, out, st, &fp);
   if (r) return r;
-  if (!units || !s_cap || !p8_cap || !md_cap) return SAGE_E_NULL;
+  if (!units || !s_cap || !p8_cap || !md_cap || !part_cap || !ro_cap || !r_cap) return SAGE_E_NULL;
   if (n_units < 1 || n_units > fp.n_units) return SAGE_E_ARG;
-  if (!aligned16(s_cap) || !aligned16(p8_cap) || !aligned16(md_cap)) return SAGE_E_ALIGN;
+  if (!aligned16(s_cap) || !aligned16(p8_cap) || !aligned16(md_cap) || !aligned16(part_cap) ||
+      !aligned16(ro_cap) || !aligned16(r_cap))
+    return SAGE_E_ALIGN;
   if ((r = device_ok())) return r;
   fp.units = units;
   fp.s_cap = s_cap;
   fp.p8_cap = p8_cap;
   fp.md_cap = md_cap;
+  fp.part_cap = part_cap;
+  fp.ro_cap = ro_cap;
+  fp.r_cap = r_cap;
   return launch_fwd(fp, s->D, n_units, true, (hipStream_t)stream) == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
 }
 

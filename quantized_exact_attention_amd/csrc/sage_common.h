@@ -55,7 +55,10 @@ struct FwdParams {
   const int32_t *units;
   int32_t *s_cap;
   uint8_t *p8_cap;
-  float *md_cap;
+  float *md_cap;                  // [unit][128][T][3]: m, 448*d, alpha after tile j
+  float *part_cap;                // [unit][128][T][D]: fresh PV partial of tile j
+  float *ro_cap;                  // [unit][128][T][D]: RO after tile j
+  float *r_cap;                   // [unit][128]: reciprocal of 448*d
 };
 
 // Workspace layout of the prep statistics, shared by the size query and the launcher.

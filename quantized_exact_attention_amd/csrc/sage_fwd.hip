@@ -266,9 +266,10 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
         pc[(w >> 2) * 32 + 8 * (v >> 2) + 4 * hi + (v & 3)] = (uint8_t)((uint32_t)pop[w] >> (8 * e));
       }
     if (hi == 0) {
-      float *md = p.md_cap + (((size_t)blockIdx.x * kBQ + row) * T + j) * 2;
+      float *md = p.md_cap + (((size_t)blockIdx.x * kBQ + row) * T + j) * 3;
       md[0] = st.m;
       md[1] = st.dsum;
+      md[2] = alpha;
     }
   }
 
@@ -288,6 +289,18 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   for (int cb = 0; cb < NS; ++cb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) st.ro[cb][v] = __builtin_fmaf(st.ro[cb][v], alpha, part[cb][v]);
+  if (CAP) {
+    // lane (hi, row) holds channels 32 cb + 8 (v / 4) + 4 hi + v % 4
+    const size_t o = (((size_t)blockIdx.x * kBQ + row) * T + j) * D;
+#pragma unroll
+    for (int cb = 0; cb < NS; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int ch = 32 * cb + 8 * (v >> 2) + 4 * hi + (v & 3);
+        p.part_cap[o + ch] = part[cb][v];
+        p.ro_cap[o + ch] = st.ro[cb][v];
+      }
+  }
 
   // tile j+1 landed (this wave's copies) and every wave is done with `cur`
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -355,8 +368,9 @@ __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_f
   const int elane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int hi = elane >> 5;
   const int n = qb * kBQ + wave * 32 + (elane & 31);
+  const float r = 1.0f / st.dsum;                 // "reciprocal" (d includes the 448)
+  if (CAP && hi == 0) p.r_cap[(size_t)blockIdx.x * kBQ + wave * 32 + (elane & 31)] = r;
   if (n < p.Nq) {
-    const float r = 1.0f / st.dsum;               // "reciprocal" (d includes the 448)
     const int b = bh / p.H, h = bh - b * p.H;
     uint16_t *orow = p.out + b * p.os[0] + h * p.os[1] + (int64_t)n * p.os[2];
     const float *vs = p.v_scale + (size_t)bh * D;

@@ -68,7 +68,7 @@ def lib() -> ctypes.CDLL:
         L.sage_attn_fwd.argtypes = [ctypes.POINTER(SageQuantC), ctypes.POINTER(SageShape), f32, vp,
                                     ctypes.POINTER(SageStrides), vp]
         L.sage_attn_fwd_capture.argtypes = [ctypes.POINTER(SageQuantC), ctypes.POINTER(SageShape), f32, vp,
-                                            ctypes.POINTER(SageStrides), vp, i32, vp, vp, vp, vp]
+                                            ctypes.POINTER(SageStrides), vp, i32, vp, vp, vp, vp, vp, vp, vp]
         L.sage_device_check.argtypes = [ctypes.c_int]
         L.sage_status_string.argtypes = [ctypes.c_int]
         L.sage_status_string.restype = ctypes.c_char_p
@@ -232,26 +232,33 @@ def sage_attn_fwd_capture(quant: SageQuant, units, sm_scale: float | None = None
                           out: torch.Tensor | None = None, stream=None):
     """Run the listed work units with checkpoint capture.
 
-    Returns (out, s_cap int32 [n,128,T*64], p8_cap uint8 [n,128,T*64],
-    md_cap float32 [n,128,T,2]) as device tensors.
+    Returns (out, caps) where caps holds device tensors: s int32 [n,128,T*64],
+    p8 uint8 [n,128,T*64], md float32 [n,128,T,3] (m, 448*d, alpha), part and ro
+    float32 [n,128,T,D], r float32 [n,128] (1/(448*d)).
     """
     out = _out_tensor(quant, out)
     dev = quant.q_codes.device
     units_t = torch.as_tensor(list(units), dtype=torch.int32).to(dev)
     n = units_t.numel()
     T = quant.T
-    s_cap = torch.zeros(n, BQ, T * BK, dtype=torch.int32, device=dev)
-    p8_cap = torch.zeros(n, BQ, T * BK, dtype=torch.uint8, device=dev)
-    md_cap = torch.zeros(n, BQ, T, 2, dtype=torch.float32, device=dev)
+    caps = {
+        "s": torch.zeros(n, BQ, T * BK, dtype=torch.int32, device=dev),
+        "p8": torch.zeros(n, BQ, T * BK, dtype=torch.uint8, device=dev),
+        "md": torch.zeros(n, BQ, T, 3, dtype=torch.float32, device=dev),
+        "part": torch.zeros(n, BQ, T, quant.D, dtype=torch.float32, device=dev),
+        "ro": torch.zeros(n, BQ, T, quant.D, dtype=torch.float32, device=dev),
+        "r": torch.zeros(n, BQ, dtype=torch.float32, device=dev),
+    }
     st = SageStrides()
     st.o = _strides3(out)
     qc = quant.c_struct()
     _check(lib().sage_attn_fwd_capture(ctypes.byref(qc), ctypes.byref(quant.shape),
                                        ctypes.c_float(0.0 if sm_scale is None else sm_scale), out.data_ptr(),
-                                       ctypes.byref(st), units_t.data_ptr(), n, s_cap.data_ptr(),
-                                       p8_cap.data_ptr(), md_cap.data_ptr(), _stream_handle(stream, dev)),
+                                       ctypes.byref(st), units_t.data_ptr(), n,
+                                       *[caps[k].data_ptr() for k in ("s", "p8", "md", "part", "ro", "r")],
+                                       _stream_handle(stream, dev)),
            "sage_attn_fwd_capture")
-    return out, s_cap, p8_cap, md_cap
+    return out, caps
 
 
 def sage_attention(q, k, v, sm_scale: float | None = None) -> torch.Tensor:

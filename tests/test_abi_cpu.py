@@ -131,10 +131,18 @@ def test_fwd_validation_before_any_hip_call(L):
     nulls.v_scale = None
     assert f(ctypes.byref(nulls), ctypes.byref(shape), 0.0, out, ctypes.byref(st), None) == -1
     cap = L.sage_attn_fwd_capture
-    assert cap(ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(st), None, 1,
-               1 << 37, 1 << 38, 1 << 39, None) == -1
-    assert cap(ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(st), 1 << 35, 0,
-               1 << 37, 1 << 38, 1 << 39, None) == -8
+    caps = [1 << 37, 1 << 38, 1 << 39, 1 << 40, 1 << 41, 1 << 42]
+    assert cap(ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(st), None, 1, *caps, None) == -1
+    assert cap(ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(st), 1 << 35, 0, *caps, None) == -8
+    for i in range(3, 6):                       # partial, RO and reciprocal buffers are required too
+        missing = list(caps)
+        missing[i] = None
+        assert cap(ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(st), 1 << 35, 1,
+                   *missing, None) == -1
+    misaligned = list(caps)
+    misaligned[4] += 4
+    assert cap(ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(st), 1 << 35, 1,
+               *misaligned, None) == -4
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
@@ -142,3 +150,4 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(sage, "LIB_PATH", "/nonexistent/libsage_attn.so")
     with pytest.raises(RuntimeError):
         sage.lib()
+
