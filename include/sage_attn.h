@@ -47,6 +47,7 @@ extern "C" {
 #define SAGE_E_DEVICE (-6)   /* no device, or the device is not gfx950 */
 #define SAGE_E_LAUNCH (-7)   /* a kernel launch failed (hipGetLastError) */
 #define SAGE_E_ARG (-8)      /* another argument is invalid */
+#define SAGE_E_SCRATCH (-9)  /* the allocation-free prep's static scratch is too small for the shape */
 
 /* problem shape */
 typedef struct sage_shape {
@@ -163,6 +164,24 @@ int sage_quant_prep(const void *q, const void *k, const void *v, const sage_shap
  */
 int sage_quant_prep_single_pass(const void *q, const void *k, const void *v, const sage_shape_t *shape,
                                 const sage_strides_t *strides, const sage_quant_t *quant, void *stream);
+
+/*
+ * Allocation-free variant of sage_quant_prep, for callers that cannot allocate
+ * device memory (code under stream/graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same kernels, arguments and results as
+ * sage_quant_prep, except that the prep's scratch (column partials and V
+ * inverses) lives in a static device array of 8 MiB per GPU, created with the
+ * library's code object and held until the process ends; quant->workspace is
+ * ignored and may be NULL.  The entry allocates nothing.  Shapes whose prep
+ * needs more scratch than that (sage_buffer_bytes of SAGE_BUF_WORKSPACE above
+ * 8 MiB; the long video workload, 24 heads of 32760 keys at D = 128, needs
+ * 4.8 MiB) return SAGE_E_SCRATCH before any HIP call.  Every call on one GPU
+ * shares that GPU's array, and each call writes before it reads all it uses:
+ * calls ordered on one stream are safe, calls that overlap in time on one GPU
+ * (different streams or host threads without ordering) race.
+ */
+int sage_quant_prep_no_alloc(const void *q, const void *k, const void *v, const sage_shape_t *shape,
+                             const sage_strides_t *strides, const sage_quant_t *quant, void *stream);
 
 /*
  * Stages 3-5 ("Experiment Log", Phase 0 stage list and Phase 1 invariants;

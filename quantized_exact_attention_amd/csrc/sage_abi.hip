@@ -4,6 +4,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <utility>
 
 #include "../../include/sage_attn.h"
@@ -99,24 +100,52 @@ size_t buffer_bytes(const sage_shape_t *s, int which) {
   }
 }
 
-int check_quant(const sage_quant_t *q) {
+// need_ws: the workspace pointer is required (every entry but the
+// allocation-free prep, which ignores it)
+int check_quant(const sage_quant_t *q, bool need_ws = true) {
   if (!q || !q->q_codes || !q->q_scale || !q->k_codes || !q->k_scale || !q->v_codes || !q->v_scale ||
-      !q->k_mean || !q->workspace)
+      !q->k_mean || (need_ws && !q->workspace))
     return SAGE_E_NULL;
-  if (!aligned16(q->q_codes) || !aligned16(q->k_codes) || !aligned16(q->v_codes) || !aligned16(q->workspace) ||
-      ((uintptr_t)q->q_scale & 3) || ((uintptr_t)q->k_scale & 3) || ((uintptr_t)q->v_scale & 3) ||
-      ((uintptr_t)q->k_mean & 3))
+  if (!aligned16(q->q_codes) || !aligned16(q->k_codes) || !aligned16(q->v_codes) ||
+      (need_ws && !aligned16(q->workspace)) || ((uintptr_t)q->q_scale & 3) || ((uintptr_t)q->k_scale & 3) ||
+      ((uintptr_t)q->v_scale & 3) || ((uintptr_t)q->k_mean & 3))
     return SAGE_E_ALIGN;
   return SAGE_OK;
 }
 
-// true if [p, p+n) overlaps any buffer of the quant set
+// true if [p, p+n) overlaps any buffer of the quant set (a NULL buffer overlaps nothing)
 bool overlaps_quant(const void *p, size_t n, const sage_quant_t *q, const sage_shape_t *s) {
   const void *bufs[SAGE_BUF_COUNT] = {q->q_codes, q->q_scale, q->k_codes, q->k_scale,
                                       q->v_codes, q->v_scale, q->k_mean, q->workspace};
   for (int i = 0; i < SAGE_BUF_COUNT; ++i)
-    if (overlap(p, n, bufs[i], buffer_bytes(s, i))) return true;
+    if (bufs[i] && overlap(p, n, bufs[i], buffer_bytes(s, i))) return true;
   return false;
+}
+
+// ---- static device scratch of the allocation-free prep entry ----------------
+// One copy of the array per GPU, created with the library's code object and
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only
+// that address is ever passed to kernels.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+__device__ __align__(256) static uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch, looked up on the first call
+// on that device.
+int scratch_address(void **ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SAGE_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SAGE_E_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return SAGE_OK;
 }
 
 int device_ok() {
@@ -174,6 +203,7 @@ const char *sage_status_string(int status) {
     case SAGE_E_DEVICE: return "no HIP device, or the device is not gfx950";
     case SAGE_E_LAUNCH: return "kernel launch failed";
     case SAGE_E_ARG: return "invalid argument";
+    case SAGE_E_SCRATCH: return "the prep needs more scratch than the allocation-free entry's static 8 MiB";
     default: return "unknown status";
   }
 }
@@ -213,12 +243,19 @@ int sage_prep_status_offset(const sage_shape_t *shape, size_t *offset) {
 
 namespace {
 
+// no_alloc: the workspace is the static device scratch instead of quant->workspace
 int quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *s, const sage_strides_t *st,
-               const sage_quant_t *quant, void *stream, bool single_pass) {
+               const sage_quant_t *quant, void *stream, bool single_pass, bool no_alloc = false) {
   int r = check_shape(s);
   if (r) return r;
   if (!q || !k || !v || !st) return SAGE_E_NULL;
-  if ((r = check_quant(quant))) return r;
+  if ((r = check_quant(quant, !no_alloc))) return r;
+  sage_quant_t qs = *quant;
+  if (no_alloc) {
+    qs.workspace = nullptr;                      // ignored; the scratch is checked below
+    if (buffer_bytes(s, SAGE_BUF_WORKSPACE) > kScratchBytes) return SAGE_E_SCRATCH;
+  }
+  quant = &qs;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || check_strides(st->q) || check_strides(st->k) ||
       check_strides(st->v))
     return SAGE_E_ALIGN;
@@ -227,6 +264,7 @@ int quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *
       overlaps_quant(v, span_bytes(s, st->v, s->Nkv), quant, s))
     return SAGE_E_ALIAS;
   if ((r = device_ok())) return r;
+  if (no_alloc && (r = scratch_address(&qs.workspace))) return r;
 
   PrepParams p;
   std::memset(&p, 0, sizeof(p));
@@ -279,6 +317,11 @@ int sage_quant_prep(const void *q, const void *k, const void *v, const sage_shap
 int sage_quant_prep_single_pass(const void *q, const void *k, const void *v, const sage_shape_t *s,
                                 const sage_strides_t *st, const sage_quant_t *quant, void *stream) {
   return quant_prep(q, k, v, s, st, quant, stream, true);
+}
+
+int sage_quant_prep_no_alloc(const void *q, const void *k, const void *v, const sage_shape_t *s,
+                             const sage_strides_t *st, const sage_quant_t *quant, void *stream) {
+  return quant_prep(q, k, v, s, st, quant, stream, false, true);
 }
 
 int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *s, float sm_scale, void *out,

@@ -36,7 +36,7 @@ def test_exports_every_header_function(L):
 
 
 def test_status_strings(L):
-    for st in range(-8, 1):
+    for st in range(-9, 1):
         assert sage.status_string(st) not in ("", "unknown status")
     assert sage.status_string(-99) == "unknown status"
 
@@ -151,3 +151,30 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     with pytest.raises(RuntimeError):
         sage.lib()
 
+
+def test_no_alloc_prep_rejects_shapes_beyond_its_scratch(L):
+    """The allocation-free prep checks its static 8 MiB scratch against the
+    shape before any HIP call; a NULL workspace is accepted there."""
+    f = L.sage_quant_prep_no_alloc
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.POINTER(sage.SageShape), ctypes.POINTER(sage.SageStrides),
+                                          ctypes.POINTER(sage.SageQuantC), ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    big = sage.SageShape(1, 64, 128, 65536, 128)
+    assert sage.sage_buffer_bytes(1, 64, 128, 65536, 128, 7) > 8 << 20
+    qc = _fake_quant()
+    qc.workspace = None
+    st = _strides(1, 64, 128, 128)
+    st.k[:] = st.v[:] = [64 * 65536 * 128, 65536 * 128, 128]
+    base = 1 << 44
+    assert f(base, base + (1 << 40), base + (1 << 41), ctypes.byref(big), ctypes.byref(st), ctypes.byref(qc),
+             None) == -9
+    # within the scratch the same call passes validation and stops at the device check (no GPU here)
+    small = sage.SageShape(1, 2, 128, 1000, 128)
+    st = _strides(1, 2, 128, 128)
+    st.k[:] = st.v[:] = [2 * 1000 * 128, 1000 * 128, 128]
+    r = f(base, base + (1 << 40), base + (1 << 41), ctypes.byref(small), ctypes.byref(st), ctypes.byref(qc), None)
+    assert r in (0, -6, -7)
+    nulls = _fake_quant()
+    nulls.k_codes = None
+    assert f(base, base + (1 << 40), base + (1 << 41), ctypes.byref(small), ctypes.byref(st), ctypes.byref(nulls),
+             None) == -1
