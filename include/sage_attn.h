@@ -230,6 +230,30 @@ int sage_attn_fwd_capture(const sage_quant_t *quant, const sage_shape_t *shape, 
                           int32_t n_units, int32_t *s_cap, uint8_t *p8_cap, float *md_cap,
                           float *part_cap, float *ro_cap, float *r_cap, void *stream);
 
+/*
+ * Race gate (tests only; the analogue of the race checks the pages require of
+ * every candidate, "Experiment Log", Phase 2A VEA-B Capability Decision):
+ * sage_quant_prep followed by sage_attn_fwd, both built with wave-uniform
+ * pseudo-random pauses (0 to 1024 cycles, drawn from `seed`, the workgroup, the
+ * wave, the site and the step) before every LDS write and read and every HBM ->
+ * LDS tile copy of the three prep launches and the forward.  With correct
+ * synchronisation the order in which waves reach those accesses cannot change
+ * any result, so every buffer of `quant` and `out` must come out bit-identical
+ * to the two normal calls.  Much slower than the normal calls.  Arguments as for
+ * sage_quant_prep and sage_attn_fwd; `out` must not overlap q, k or v; seed 0
+ * returns SAGE_E_ARG.
+ */
+int sage_race_gate(const void *q, const void *k, const void *v, const sage_shape_t *shape,
+                   const sage_strides_t *strides, const sage_quant_t *quant, float sm_scale, void *out,
+                   uint32_t seed, void *stream);
+
+/* Diagnostics: one lane of one workgroup writes the shader-clock counter
+ * (s_memtime) to dst[0] and the constant 100 MHz counter (s_memrealtime) to
+ * dst[1] (device uint64 [2], 8-byte aligned) when `stream` reaches the call.
+ * Two samples around a timed region give the average shader clock over it:
+ * (dst'[0] - dst[0]) / (dst'[1] - dst[1]) * 100 MHz. */
+int sage_clock_sample(uint64_t *dst, void *stream);
+
 /* SAGE_OK if `device` is a gfx950 GPU, else SAGE_E_DEVICE (one HIP query). */
 int sage_device_check(int device);
 

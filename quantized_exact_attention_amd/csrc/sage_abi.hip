@@ -188,9 +188,27 @@ int fill_fwd(const sage_quant_t *q, const sage_shape_t *s, float sm_scale, void 
   return SAGE_OK;
 }
 
+// One lane records the shader-clock counter (s_memtime) and the constant
+// 100 MHz counter (s_memrealtime).
+__global__ void k_clock_sample(uint64_t *dst) {
+  if (threadIdx.x == 0) {
+    dst[0] = __builtin_amdgcn_s_memtime();
+    dst[1] = __builtin_amdgcn_s_memrealtime();
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+int sage_clock_sample(uint64_t *dst, void *stream) {
+  if (!dst) return SAGE_E_NULL;
+  if (((uintptr_t)dst & 7u) != 0) return SAGE_E_ALIGN;
+  int r = device_ok();
+  if (r) return r;
+  hipLaunchKernelGGL(k_clock_sample, dim3(1), dim3(64), 0, (hipStream_t)stream, dst);
+  return hipGetLastError() == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
+}
 
 const char *sage_status_string(int status) {
   switch (status) {
@@ -243,9 +261,11 @@ int sage_prep_status_offset(const sage_shape_t *shape, size_t *offset) {
 
 namespace {
 
-// no_alloc: the workspace is the static device scratch instead of quant->workspace
+// no_alloc: the workspace is the static device scratch instead of quant->workspace;
+// race_seed: nonzero runs the race-gate build of the three launches
 int quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *s, const sage_strides_t *st,
-               const sage_quant_t *quant, void *stream, bool single_pass, bool no_alloc = false) {
+               const sage_quant_t *quant, void *stream, bool single_pass, bool no_alloc = false,
+               uint32_t race_seed = 0) {
   int r = check_shape(s);
   if (r) return r;
   if (!q || !k || !v || !st) return SAGE_E_NULL;
@@ -302,6 +322,7 @@ int quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *
   const int groups = ceil_div(s->Nkv, kFusedRows(s->D));
   // G = 0: statistics, finalize and quantization launches
   p.G = single_pass && groups <= kFusedMaxGroups ? groups : 0;
+  p.race_seed = race_seed;
   return launch_prep(p, (hipStream_t)stream) == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
 }
 
@@ -330,7 +351,8 @@ int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *s, float sm_sca
   int r = fill_fwd(quant, s, sm_scale, out, st, &fp);
   if (r) return r;
   if ((r = device_ok())) return r;
-  return launch_fwd(fp, s->D, fp.n_units, false, (hipStream_t)stream) == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
+  return launch_fwd(fp, s->D, fp.n_units, false, false, (hipStream_t)stream) == hipSuccess ? SAGE_OK
+                                                                                            : SAGE_E_LAUNCH;
 }
 
 int sage_attn_fwd_capture(const sage_quant_t *quant, const sage_shape_t *s, float sm_scale, void *out,
@@ -353,7 +375,23 @@ int sage_attn_fwd_capture(const sage_quant_t *quant, const sage_shape_t *s, floa
   fp.part_cap = part_cap;
   fp.ro_cap = ro_cap;
   fp.r_cap = r_cap;
-  return launch_fwd(fp, s->D, n_units, true, (hipStream_t)stream) == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
+  return launch_fwd(fp, s->D, n_units, true, false, (hipStream_t)stream) == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
+}
+
+int sage_race_gate(const void *q, const void *k, const void *v, const sage_shape_t *s, const sage_strides_t *st,
+                   const sage_quant_t *quant, float sm_scale, void *out, uint32_t seed, void *stream) {
+  if (seed == 0) return SAGE_E_ARG;
+  FwdParams fp;
+  int r = fill_fwd(quant, s, sm_scale, out, st, &fp);
+  if (r) return r;
+  if (out && (overlap(out, span_bytes(s, st->o, s->Nq), q, span_bytes(s, st->q, s->Nq)) ||
+              overlap(out, span_bytes(s, st->o, s->Nq), k, span_bytes(s, st->k, s->Nkv)) ||
+              overlap(out, span_bytes(s, st->o, s->Nq), v, span_bytes(s, st->v, s->Nkv))))
+    return SAGE_E_ALIAS;
+  if ((r = quant_prep(q, k, v, s, st, quant, stream, false, false, seed))) return r;
+  fp.race_seed = seed;
+  return launch_fwd(fp, s->D, fp.n_units, false, true, (hipStream_t)stream) == hipSuccess ? SAGE_OK
+                                                                                          : SAGE_E_LAUNCH;
 }
 
 }  // extern "C"

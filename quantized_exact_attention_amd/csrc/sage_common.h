@@ -37,6 +37,7 @@ struct PrepParams {
   double *ws_asum;                // single-pass path: [B*H][D] K column sums (atomic, exact)
   uint32_t *ws_amax;              // single-pass path: [B*H][D] V column max |v| (float bits, atomic max)
   int G;                          // single-pass path: K/V workgroups per (b,h); 0 selects three launches
+  uint32_t race_seed;             // nonzero: the race-gate build of the three launches (tests only)
 };
 
 struct FwdParams {
@@ -59,7 +60,29 @@ struct FwdParams {
   float *part_cap;                // [unit][128][T][D]: fresh PV partial of tile j
   float *ro_cap;                  // [unit][128][T][D]: RO after tile j
   float *r_cap;                   // [unit][128]: reciprocal of 448*d
+  uint32_t race_seed;             // race-gate build only
 };
+
+// Race gate (test builds only).  A wave-uniform pseudo-random pause of 0, 64,
+// 256 or 1024 cycles, drawn from (seed, workgroup, wave, site, step), placed
+// before the LDS writes and reads (and the HBM -> LDS copies) of a kernel: with
+// correct synchronisation the results cannot depend on the order in which
+// waves reach them, so a race-gate run must give the normal build's bits.
+__device__ __forceinline__ void race_pause(uint32_t seed, uint32_t site, uint32_t step) {
+  uint32_t h = seed ^ (blockIdx.x * 0x9E3779B1u) ^ (blockIdx.y * 0x85EBCA77u) ^ ((threadIdx.x >> 6) * 0xC2B2AE3Du) ^
+               (site * 0x27D4EB2Fu) ^ (step * 0x165667B1u);
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  h *= 0x297A2D39u;
+  h ^= h >> 15;
+  switch (__builtin_amdgcn_readfirstlane(h) & 3u) {
+    case 1: __builtin_amdgcn_s_sleep(1); break;
+    case 2: __builtin_amdgcn_s_sleep(4); break;
+    case 3: __builtin_amdgcn_s_sleep(16); break;
+    default: break;
+  }
+}
 
 // Workspace layout of the prep statistics, shared by the size query and the launcher.
 inline size_t ws_ksum_bytes(int BH, int nchunk, int D) { return (size_t)BH * nchunk * D * sizeof(double); }
@@ -79,6 +102,7 @@ constexpr int kFusedMaxGroups = 256;
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 hipError_t launch_prep(const PrepParams &p, hipStream_t stream);
-hipError_t launch_fwd(const FwdParams &p, int D, int grid, bool capture, hipStream_t stream);
+// race: the race-gate build (p.race_seed nonzero; not with capture)
+hipError_t launch_fwd(const FwdParams &p, int D, int grid, bool capture, bool race, hipStream_t stream);
 
 }  // namespace sage

@@ -152,7 +152,7 @@ struct FwdState {
 // One 64-key tile of the ordered traversal for one wavefront (32 query rows).
 // `cur` holds tile j; tile j+1 is copied into `nxt` meanwhile.  Ends with the
 // workgroup barrier that publishes `nxt` and retires `cur`.
-template <int D, bool CAP>
+template <int D, bool CAP, bool RACE>
 __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, const v4i *qop, float sq, int j,
                                           const uint8_t *cur, uint8_t *nxt, const int8_t *kg, const uint8_t *vg,
                                           const float *ksc, int wave, int lane, int row) {
@@ -160,12 +160,14 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   constexpr int TILE = kBK * D;
   const int T = p.T;
   const int hi = lane >> 5;   // which 4-key group of each 8 this lane holds
+  if (RACE) race_pause(p.race_seed, 0, j);
   if (j + 1 < T) issue_tile<D>(nxt, kg, vg, j + 1, wave, lane);
   const uint8_t *kl = cur + lane * 16;        // this lane's 16 bytes of every 1 KiB operand block
   const uint8_t *vl = kl + TILE;
 
   // ---- S^T = K_j . Q^T (int32, exact, offset by kScoreBias) ----
   __builtin_amdgcn_s_setprio(kPrioMatrix);
+  if (RACE) race_pause(p.race_seed, 1, j);
   v16i sacc[2];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -275,6 +277,7 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
 
   // ---- partial^T = V_j^T . P8^T (FP32, fresh), then RO = RO * alpha + partial ----
   __builtin_amdgcn_s_setprio(kPrioMatrix);
+  if (RACE) race_pause(p.race_seed, 2, j);
   const v16f zero16 = {};
   v16f part[NS];
 #pragma unroll
@@ -307,7 +310,7 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   __syncthreads();
 }
 
-template <int D, bool CAP>
+template <int D, bool CAP, bool RACE>
 __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_fwd(FwdParams p) {
   constexpr int NS = D / 32;                 // INT8 k-steps per key row == PV row blocks
   constexpr int TILE = kBK * D;              // bytes of one K (or V) tile
@@ -331,6 +334,7 @@ __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_f
   const uint8_t *vg = p.v_codes + (size_t)bh * T * TILE;
   const float *ksc = p.k_scale + (size_t)bh * T;
 
+  if (RACE) race_pause(p.race_seed, 3, 0);
   issue_tile<D>(lds_a, kg, vg, 0, wave, lane);
 
   // Q^T operand (B of the INT8 product) for this wave's 32 rows, kept in registers.
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_f
   for (int j = 0; j < T; ++j) {
     uint8_t *cur = (j & 1) ? lds_b : lds_a;
     uint8_t *nxt = (j & 1) ? lds_a : lds_b;
-    tile_step<D, CAP>(p, st, qop, sq, j, cur, nxt, kg, vg, ksc, wave, lane, row);
+    tile_step<D, CAP, RACE>(p, st, qop, sq, j, cur, nxt, kg, vg, ksc, wave, lane, row);
   }
 
   __builtin_amdgcn_s_setprio(3);                 // finish and free the slot quickly
@@ -392,13 +396,15 @@ __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_f
   }
 }
 
-hipError_t launch_fwd(const FwdParams &p, int D, int grid, bool capture, hipStream_t st) {
+hipError_t launch_fwd(const FwdParams &p, int D, int grid, bool capture, bool race, hipStream_t st) {
   if (D == 128) {
-    if (capture) hipLaunchKernelGGL((k_attn_fwd<128, true>), dim3(grid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((k_attn_fwd<128, false>), dim3(grid), dim3(256), 0, st, p);
+    if (capture) hipLaunchKernelGGL((k_attn_fwd<128, true, false>), dim3(grid), dim3(256), 0, st, p);
+    else if (race) hipLaunchKernelGGL((k_attn_fwd<128, false, true>), dim3(grid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_attn_fwd<128, false, false>), dim3(grid), dim3(256), 0, st, p);
   } else {
-    if (capture) hipLaunchKernelGGL((k_attn_fwd<64, true>), dim3(grid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((k_attn_fwd<64, false>), dim3(grid), dim3(256), 0, st, p);
+    if (capture) hipLaunchKernelGGL((k_attn_fwd<64, true, false>), dim3(grid), dim3(256), 0, st, p);
+    else if (race) hipLaunchKernelGGL((k_attn_fwd<64, false, true>), dim3(grid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_attn_fwd<64, false, false>), dim3(grid), dim3(256), 0, st, p);
   }
   return hipGetLastError();
 }

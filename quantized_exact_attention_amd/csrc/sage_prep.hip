@@ -25,14 +25,18 @@ __device__ __forceinline__ void unpack8(const uint4 &x, float *f) {
 }
 
 // Max of a non-negative float over the 256-thread block (bit order == value order).
-__device__ __forceinline__ float block_max_nonneg(float x, float *red) {
+// RACE: the race-gate build (pauses before the LDS write and read).
+template <bool RACE = false>
+__device__ __forceinline__ float block_max_nonneg(float x, float *red, uint32_t seed = 0) {
   uint32_t u = __float_as_uint(x);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) u = max(u, (uint32_t)__shfl_xor((int)u, o, 64));
   const int w = threadIdx.x >> 6;
   __syncthreads();
+  if (RACE) race_pause(seed, 10, 0);
   if ((threadIdx.x & 63) == 0) red[w] = __uint_as_float(u);
   __syncthreads();
+  if (RACE) race_pause(seed, 11, 0);
   float r = red[0];
 #pragma unroll
   for (int i = 1; i < 4; ++i) r = fmaxf(r, red[i]);
@@ -74,7 +78,7 @@ struct StatsSmem {
 
 constexpr int kBatch = 8;
 
-template <int D>
+template <int D, bool RACE>
 __device__ __forceinline__ void prep_stats_block(const PrepParams &p, int chunk, int bh, StatsSmem<D> &sm) {
   constexpr int CG = StatsSmem<D>::CG, TL = StatsSmem<D>::TL, RPT = kStatChunk / TL;
   static_assert(RPT % kBatch == 0, "rows per thread must be a multiple of the load batch");
@@ -113,9 +117,11 @@ __device__ __forceinline__ void prep_stats_block(const PrepParams &p, int chunk,
       }
     }
   }
+  if (RACE) race_pause(p.race_seed, 0, chunk);
 #pragma unroll
   for (int e = 0; e < 8; ++e) { s_sum[tl][cg * 8 + e] = acc[e]; s_max[tl][cg * 8 + e] = vmx[e]; }
   __syncthreads();
+  if (RACE) race_pause(p.race_seed, 1, chunk);
   for (int c = threadIdx.x; c < D; c += 256) {
     double s = 0.0;
     float mx = 0.f;
@@ -129,7 +135,7 @@ __device__ __forceinline__ void prep_stats_block(const PrepParams &p, int chunk,
 // ---- 2. per (b,h, 16 channels): K mean, V channel scale and inverse ------------
 // 256 threads: channel 16*blockIdx.y + t % 16, chunk group t / 16; the partial
 // sums are exact, so their order does not matter.
-template <int D>
+template <int D, bool RACE>
 __global__ __launch_bounds__(256) void k_prep_finalize(PrepParams p) {
   constexpr int NG = 16, U = 4;
   __shared__ double s_sum[NG][16];
@@ -154,9 +160,11 @@ __global__ __launch_bounds__(256) void k_prep_finalize(PrepParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) { s += ps[u]; mx = fmaxf(mx, pm[u]); }
   }
+  if (RACE) race_pause(p.race_seed, 2, 0);
   s_sum[g][cl] = s;
   s_max[g][cl] = mx;
   __syncthreads();
+  if (RACE) race_pause(p.race_seed, 3, 0);
   if (g == 0) {
 #pragma unroll
     for (int i = 1; i < NG; ++i) { s += s_sum[i][cl]; mx = fmaxf(mx, s_max[i][cl]); }
@@ -171,9 +179,9 @@ __global__ __launch_bounds__(256) void k_prep_finalize(PrepParams p) {
 // 8 * (t % (D/8)) (the same for every i, since 256 is a multiple of D/8), so a
 // wave reads whole rows.  The raw bf16 words stay in registers and are unpacked
 // again for the codes; each unit becomes 8 bytes of a 16-byte operand unit.
-template <int D, int R, bool SMOOTH>
+template <int D, int R, bool SMOOTH, bool RACE = false>
 __device__ __forceinline__ void quant_i8_rows(const uint16_t *base, int64_t rs, int nvalid, const float *mean,
-                                              int8_t *dst, float *scale_out, float *red) {
+                                              int8_t *dst, float *scale_out, float *red, uint32_t seed = 0) {
   constexpr int UPR = D / 8, UPT = R * UPR / 256;
   static_assert(256 % UPR == 0 && UPT >= 1, "unit mapping");
   const int c8 = threadIdx.x % UPR, r0 = threadIdx.x / UPR;
@@ -202,7 +210,7 @@ __device__ __forceinline__ void quant_i8_rows(const uint16_t *base, int64_t rs, 
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
   }
-  amax = block_max_nonneg(amax, red);
+  amax = block_max_nonneg<RACE>(amax, red, seed);
   const float inv = amax > 0.f ? 127.0f / amax : 0.f;
   if (threadIdx.x == 0) *scale_out = amax > 0.f ? amax / 127.0f : 0.f;
 #pragma unroll
@@ -217,12 +225,13 @@ __device__ __forceinline__ void quant_i8_rows(const uint16_t *base, int64_t rs, 
   }
 }
 
-template <int D>
+template <int D, bool RACE = false>
 __device__ __forceinline__ void quant_q_block(const PrepParams &p, int qb, int bh, float *red) {
   const int b = bh / p.H, h = bh - b * p.H;
   const uint16_t *base = p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)qb * kBQ * p.qs[2];
-  quant_i8_rows<D, kBQ, false>(base, p.qs[2], min(kBQ, p.Nq - qb * kBQ), nullptr,
-                               p.q_codes + ((size_t)bh * p.nqb + qb) * kBQ * D, p.q_scale + bh * p.nqb + qb, red);
+  quant_i8_rows<D, kBQ, false, RACE>(base, p.qs[2], min(kBQ, p.Nq - qb * kBQ), nullptr,
+                                     p.q_codes + ((size_t)bh * p.nqb + qb) * kBQ * D, p.q_scale + bh * p.nqb + qb,
+                                     red, p.race_seed);
 }
 
 // ---- 4. one 64-key tile: K smoothing + per-tile INT8, and per-channel E4M3FN V -
@@ -236,7 +245,7 @@ struct KVTileSmem {
   float red[4];
 };
 
-template <int D>
+template <int D, bool RACE>
 __device__ __forceinline__ void quant_kv_tile(const PrepParams &p, int j, int bh, KVTileSmem<D> &sm) {
   constexpr int VU = D / 8, VUPT = kBK * VU / 256;    // V: 8-channel loads per thread
   constexpr int NUNIT = (D / 32) * 2 * 64;            // 16-byte V output units per tile
@@ -250,6 +259,7 @@ __device__ __forceinline__ void quant_kv_tile(const PrepParams &p, int j, int bh
     vraw[i] = make_uint4(0, 0, 0, 0);
     if (r < nvalid) vraw[i] = *(const uint4 *)(vbase + (int64_t)r * p.vs[2] + c8 * 8);
   }
+  if (RACE) race_pause(p.race_seed, 4, j);
 #pragma unroll
   for (int i = 0; i < VUPT; ++i) {
     const int u = i * 256 + threadIdx.x, r = u / VU, c8 = u % VU;
@@ -258,9 +268,10 @@ __device__ __forceinline__ void quant_kv_tile(const PrepParams &p, int j, int bh
 
   // K: ks = fp32(K - mean), then the tile's INT8 scale and codes; the barriers of
   // its block maximum also publish the V tile in LDS.
-  quant_i8_rows<D, kBK, true>(p.k + b * p.ks[0] + h * p.ks[1] + (int64_t)j * kBK * p.ks[2], p.ks[2], nvalid,
-                              p.k_mean + (size_t)bh * D, p.k_codes + ((size_t)bh * p.T + j) * kBK * D,
-                              p.k_scale + (size_t)bh * p.T + j, sm.red);
+  quant_i8_rows<D, kBK, true, RACE>(p.k + b * p.ks[0] + h * p.ks[1] + (int64_t)j * kBK * p.ks[2], p.ks[2],
+                                    nvalid, p.k_mean + (size_t)bh * D, p.k_codes + ((size_t)bh * p.T + j) * kBK * D,
+                                    p.k_scale + (size_t)bh * p.T + j, sm.red, p.race_seed);
+  if (RACE) race_pause(p.race_seed, 5, j);
 
   // V: code = E4M3FN_RNE(fp32(v * vinv_c)).
   const float *vinv = p.ws_vinv + (size_t)bh * D;
@@ -520,18 +531,18 @@ __global__ __launch_bounds__(256) void k_prep_clear(uint32_t *w, int n) {
 // ---- launches: [stats | Q quant] -> finalize -> [K and V quant per tile] --------
 // Q quantization does not depend on the statistics, so it shares the first
 // launch; one workgroup of the last launch quantizes the K and V rows of a tile.
-template <int D>
+template <int D, bool RACE>
 __global__ __launch_bounds__(256) void k_prep_pass1(PrepParams p) {
   __shared__ StatsSmem<D> sm;
   const int bh = blockIdx.y;
-  if ((int)blockIdx.x < p.nchunk) prep_stats_block<D>(p, blockIdx.x, bh, sm);
-  else quant_q_block<D>(p, blockIdx.x - p.nchunk, bh, (float *)&sm);
+  if ((int)blockIdx.x < p.nchunk) prep_stats_block<D, RACE>(p, blockIdx.x, bh, sm);
+  else quant_q_block<D, RACE>(p, blockIdx.x - p.nchunk, bh, (float *)&sm);
 }
 
-template <int D>
+template <int D, bool RACE>
 __global__ __launch_bounds__(256) void k_prep_pass2(PrepParams p) {
   __shared__ KVTileSmem<D> sm;
-  quant_kv_tile<D>(p, blockIdx.x, blockIdx.y, sm);
+  quant_kv_tile<D, RACE>(p, blockIdx.x, blockIdx.y, sm);
 }
 
 template <int D>
@@ -543,9 +554,15 @@ static hipError_t launch_prep_d(const PrepParams &p, hipStream_t st) {
     hipLaunchKernelGGL(k_prep_fused<D>, dim3(BH * p.G + BH * p.nqb), dim3(256), 0, st, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_prep_pass1<D>, dim3(p.nchunk + p.nqb, BH), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(k_prep_finalize<D>, dim3(BH, D / 16), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(k_prep_pass2<D>, dim3(p.T, BH), dim3(256), 0, st, p);
+  if (p.race_seed) {
+    hipLaunchKernelGGL((k_prep_pass1<D, true>), dim3(p.nchunk + p.nqb, BH), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_prep_finalize<D, true>), dim3(BH, D / 16), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_prep_pass2<D, true>), dim3(p.T, BH), dim3(256), 0, st, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((k_prep_pass1<D, false>), dim3(p.nchunk + p.nqb, BH), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((k_prep_finalize<D, false>), dim3(BH, D / 16), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((k_prep_pass2<D, false>), dim3(p.T, BH), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

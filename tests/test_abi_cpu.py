@@ -178,3 +178,19 @@ def test_no_alloc_prep_rejects_shapes_beyond_its_scratch(L):
     nulls.k_codes = None
     assert f(base, base + (1 << 40), base + (1 << 41), ctypes.byref(small), ctypes.byref(st), ctypes.byref(nulls),
              None) == -1
+
+
+def test_race_gate_validation_before_any_hip_call(L):
+    f = L.sage_race_gate
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.POINTER(sage.SageShape), ctypes.POINTER(sage.SageStrides),
+                                          ctypes.POINTER(sage.SageQuantC), ctypes.c_float, ctypes.c_void_p,
+                                          ctypes.c_uint32, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    shape = sage.SageShape(1, 2, 100, 100, 64)
+    st = _strides(1, 2, 100, 64)
+    qc = _fake_quant()
+    q, k, v, out = 1 << 44, (1 << 44) + (1 << 36), (1 << 44) + (2 << 36), (1 << 44) + (3 << 36)
+    assert f(q, k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(qc), 0.0, out, 0, None) == -8
+    assert f(q, k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(qc), 0.0, q, 5, None) == -5
+    assert f(q, k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(qc), 0.0, None, 5, None) == -1
+    assert f(q, k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(qc), 0.0, out, 5, None) in (-6, -7, 0)
