@@ -24,6 +24,8 @@ sys.path.insert(0, ROOT)
 
 MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense INT8 (POP/s) and FP8 (FLOP/s) peak, 5.0 P
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+# matrix-core throughput per clock for INT8 and FP8: 256 CUs x 4 SIMDs x 2048 ops
+MFMA_OPS_PER_CLOCK = 256 * 4 * 2048
 
 
 def kernel_source_hash() -> str:
@@ -53,6 +55,28 @@ def measured_traffic(workload: str):
     if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
         return None
     return entry.get("bytes_per_launch")
+
+
+def shader_clock_ghz(samples):
+    """Average shader clock per compute unit between two clock samples
+    ([2, n, 4]: counter, 100 MHz counter, XCD id, hardware id): each unit's
+    counter delta over the 100 MHz delta; median, min and max over the units
+    seen in both samples (the shader-clock counter is kept per unit; a unit is
+    the XCD id with the CU, shader-array and shader-engine fields, bits 8-14,
+    of the hardware id)."""
+    import numpy as np
+    first = {}
+    for row in samples[0]:
+        first.setdefault((int(row[2]), (int(row[3]) >> 8) & 0x7F), row)
+    ghz = []
+    for row in samples[1]:
+        a = first.get((int(row[2]), (int(row[3]) >> 8) & 0x7F))
+        if a is not None and row[1] > a[1]:
+            ghz.append((int(row[0]) - int(a[0])) / (int(row[1]) - int(a[1])) * 0.1)
+    if not ghz:
+        return None
+    return {"median": float(np.median(ghz)), "min": float(min(ghz)), "max": float(max(ghz)),
+            "units": len(set((int(r[2]), (int(r[3]) >> 8) & 0x7F) for r in samples[1]))}
 
 
 def _oracle_blocks(args):
@@ -197,16 +221,20 @@ def main():
     print("bench: warmup done, timing %d steps" % args.steps, file=sys.stderr, flush=True)
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    clk = torch.zeros(2, sage.CLOCK_SAMPLES, 4, dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    sage.sage_clock_sample(clk[0], stream)
     for i in range(args.steps):
         ev[i][0].record(stream)
         sage.sage_quant_prep(qd, kd, vd, out=quant)
         ev[i][1].record(stream)
         sage.sage_attn_fwd(quant, out=out)
         ev[i][2].record(stream)
+    sage.sage_clock_sample(clk[1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk = shader_clock_ghz(clk.cpu().numpy())
     step_ms = [e[0].elapsed_time(e[2]) for e in ev]
     prep_ms = [e[0].elapsed_time(e[1]) for e in ev]
     fwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
@@ -246,6 +274,13 @@ def main():
             "frac": achieved / MFMA_PEAK_TFLOPS,
             "traffic": measured_traffic(w.name),
         },
+        # average shader clock over the timed steps (s_memtime against the
+        # 100 MHz counter, sampled on the launch stream before and after), and
+        # the forward's matrix-core busy fraction that follows from its
+        # algorithmic matrix work, its average duration and that clock
+        "sustained_sclk_ghz": sclk,
+        "fwd_mfma_busy_derived": ((w.flops / MFMA_OPS_PER_CLOCK) / (fwd_avg * 1e-3 * sclk["median"] * 1e9)
+                                  if sclk else None),
         "cpu_baseline": None,
     }
     # The prep (three launches) is an HBM-bound stream: bytes of its two-pass
@@ -270,6 +305,18 @@ def main():
             sp_ms.append((a, b))
     torch.cuda.synchronize()
     res["prep_single_pass_ms_p50"] = statistics.median(a.elapsed_time(b) for a, b in sp_ms)
+    # The paired forward schedule (three Q blocks per workgroup share one K/V
+    # stream; same output), timed apart from the step.
+    pf_ms = []
+    for i in range(args.warmup + args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        sage.sage_attn_fwd(quant, out=out, paired=True)
+        b.record(stream)
+        if i >= args.warmup:
+            pf_ms.append((a, b))
+    torch.cuda.synchronize()
+    res["fwd_paired_ms_p50"] = statistics.median(a.elapsed_time(b) for a, b in pf_ms)
     if w.name == "single_tile":
         # the pages quote this fixture's forward both batched and as single
         # launches (2,000 samples); time single launches the same way: one

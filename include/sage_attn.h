@@ -208,6 +208,21 @@ int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *shape, float sm
                   const sage_strides_t *strides, void *stream);
 
 /*
+ * sage_attn_fwd with the paired schedule (the analogue of the pages' temporal
+ * pairing, "Experiment Log", Closed Prior Work, and "Experiment Registry",
+ * Complete Registry): each workgroup takes three consecutive 128-row Q blocks
+ * of one (b,h) (twelve wavefronts) and streams every K/V tile through LDS once
+ * for all three, instead of once per block.  Same arithmetic per query row,
+ * so the output is bit-identical to sage_attn_fwd.  Arguments, layouts,
+ * ownership and errors as for sage_attn_fwd.  Slower than sage_attn_fwd on the
+ * workloads measured: the K/V re-reads it removes are L2 hits there, and the
+ * three wavefronts that share a SIMD then run in step behind one barrier
+ * instead of overlapping their matrix and vector phases.
+ */
+int sage_attn_fwd_paired(const sage_quant_t *quant, const sage_shape_t *shape, float sm_scale, void *out,
+                         const sage_strides_t *strides, void *stream);
+
+/*
  * Diagnostic variant of sage_attn_fwd (same kernel source, capture build):
  * runs only the n_units work units listed in `units` (device int32 array;
  * unit = ((b*H + h) * NQB + qblock)) and, besides their O rows, writes all
@@ -247,11 +262,14 @@ int sage_race_gate(const void *q, const void *k, const void *v, const sage_shape
                    const sage_strides_t *strides, const sage_quant_t *quant, float sm_scale, void *out,
                    uint32_t seed, void *stream);
 
-/* Diagnostics: one lane of one workgroup writes the shader-clock counter
- * (s_memtime) to dst[0] and the constant 100 MHz counter (s_memrealtime) to
- * dst[1] (device uint64 [2], 8-byte aligned) when `stream` reaches the call.
- * Two samples around a timed region give the average shader clock over it:
- * (dst'[0] - dst[0]) / (dst'[1] - dst[1]) * 100 MHz. */
+/* Diagnostics: when `stream` reaches the call, SAGE_CLOCK_SAMPLES workgroups
+ * each write to dst[4*i .. 4*i+3] (device uint64, 8-byte aligned): the
+ * shader-clock counter (s_memtime, kept per compute unit), the constant
+ * 100 MHz counter (s_memrealtime), the XCD id and the compute unit's hardware
+ * id (HW_REG_HW_ID; bits 8-14 name the unit inside its XCD).  Two
+ * samples around a timed region, matched by (XCD, unit), give each unit's
+ * average shader clock over it: delta(counter) / delta(100 MHz counter) * 100 MHz. */
+#define SAGE_CLOCK_SAMPLES 2048
 int sage_clock_sample(uint64_t *dst, void *stream);
 
 /* SAGE_OK if `device` is a gfx950 GPU, else SAGE_E_DEVICE (one HIP query). */

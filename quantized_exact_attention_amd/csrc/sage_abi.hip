@@ -188,12 +188,18 @@ int fill_fwd(const sage_quant_t *q, const sage_shape_t *s, float sm_scale, void 
   return SAGE_OK;
 }
 
-// One lane records the shader-clock counter (s_memtime) and the constant
-// 100 MHz counter (s_memrealtime).
+// Every workgroup records, from one lane: the shader-clock counter
+// (s_memtime, kept per compute unit), the constant 100 MHz counter
+// (s_memrealtime), the XCD id (HW_REG_XCC_ID) and the hardware id of its
+// compute unit (HW_REG_HW_ID).  SAGE_CLOCK_SAMPLES workgroups cover every
+// compute unit with high probability, so two samples can be matched unit by unit.
 __global__ void k_clock_sample(uint64_t *dst) {
   if (threadIdx.x == 0) {
-    dst[0] = __builtin_amdgcn_s_memtime();
-    dst[1] = __builtin_amdgcn_s_memrealtime();
+    uint64_t *d = dst + 4 * (size_t)blockIdx.x;
+    d[0] = __builtin_amdgcn_s_memtime();
+    d[1] = __builtin_amdgcn_s_memrealtime();
+    d[2] = __builtin_amdgcn_s_getreg((15 << 11) | 20);   // HW_REG_XCC_ID
+    d[3] = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_REG_HW_ID
   }
 }
 
@@ -206,7 +212,7 @@ int sage_clock_sample(uint64_t *dst, void *stream) {
   if (((uintptr_t)dst & 7u) != 0) return SAGE_E_ALIGN;
   int r = device_ok();
   if (r) return r;
-  hipLaunchKernelGGL(k_clock_sample, dim3(1), dim3(64), 0, (hipStream_t)stream, dst);
+  hipLaunchKernelGGL(k_clock_sample, dim3(SAGE_CLOCK_SAMPLES), dim3(64), 0, (hipStream_t)stream, dst);
   return hipGetLastError() == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
 }
 
@@ -351,8 +357,18 @@ int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *s, float sm_sca
   int r = fill_fwd(quant, s, sm_scale, out, st, &fp);
   if (r) return r;
   if ((r = device_ok())) return r;
-  return launch_fwd(fp, s->D, fp.n_units, false, false, (hipStream_t)stream) == hipSuccess ? SAGE_OK
-                                                                                            : SAGE_E_LAUNCH;
+  return launch_fwd(fp, s->D, fp.n_units, false, false, false, (hipStream_t)stream) == hipSuccess ? SAGE_OK
+                                                                                                   : SAGE_E_LAUNCH;
+}
+
+int sage_attn_fwd_paired(const sage_quant_t *quant, const sage_shape_t *s, float sm_scale, void *out,
+                         const sage_strides_t *st, void *stream) {
+  FwdParams fp;
+  int r = fill_fwd(quant, s, sm_scale, out, st, &fp);
+  if (r) return r;
+  if ((r = device_ok())) return r;
+  return launch_fwd(fp, s->D, fp.n_units, false, false, true, (hipStream_t)stream) == hipSuccess ? SAGE_OK
+                                                                                                  : SAGE_E_LAUNCH;
 }
 
 int sage_attn_fwd_capture(const sage_quant_t *quant, const sage_shape_t *s, float sm_scale, void *out,
@@ -375,7 +391,8 @@ int sage_attn_fwd_capture(const sage_quant_t *quant, const sage_shape_t *s, floa
   fp.part_cap = part_cap;
   fp.ro_cap = ro_cap;
   fp.r_cap = r_cap;
-  return launch_fwd(fp, s->D, n_units, true, false, (hipStream_t)stream) == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
+  return launch_fwd(fp, s->D, n_units, true, false, false, (hipStream_t)stream) == hipSuccess ? SAGE_OK
+                                                                                               : SAGE_E_LAUNCH;
 }
 
 int sage_race_gate(const void *q, const void *k, const void *v, const sage_shape_t *s, const sage_strides_t *st,
@@ -390,8 +407,8 @@ int sage_race_gate(const void *q, const void *k, const void *v, const sage_shape
     return SAGE_E_ALIAS;
   if ((r = quant_prep(q, k, v, s, st, quant, stream, false, false, seed))) return r;
   fp.race_seed = seed;
-  return launch_fwd(fp, s->D, fp.n_units, false, true, (hipStream_t)stream) == hipSuccess ? SAGE_OK
-                                                                                          : SAGE_E_LAUNCH;
+  return launch_fwd(fp, s->D, fp.n_units, false, true, false, (hipStream_t)stream) == hipSuccess ? SAGE_OK
+                                                                                                 : SAGE_E_LAUNCH;
 }
 
 }  // extern "C"

@@ -102,7 +102,12 @@ constexpr int kFusedMaxGroups = 256;
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 hipError_t launch_prep(const PrepParams &p, hipStream_t stream);
-// race: the race-gate build (p.race_seed nonzero; not with capture)
-hipError_t launch_fwd(const FwdParams &p, int D, int grid, bool capture, bool race, hipStream_t stream);
+// Q blocks per workgroup of the paired forward schedule
+constexpr int kPairedBlocks = 3;
+
+// race: the race-gate build (p.race_seed nonzero); paired: the paired schedule;
+// at most one of capture, race and paired
+hipError_t launch_fwd(const FwdParams &p, int D, int grid, bool capture, bool race, bool paired,
+                      hipStream_t stream);
 
 }  // namespace sage

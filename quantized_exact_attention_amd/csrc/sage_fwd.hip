@@ -152,7 +152,7 @@ struct FwdState {
 // One 64-key tile of the ordered traversal for one wavefront (32 query rows).
 // `cur` holds tile j; tile j+1 is copied into `nxt` meanwhile.  Ends with the
 // workgroup barrier that publishes `nxt` and retires `cur`.
-template <int D, bool CAP, bool RACE>
+template <int D, bool CAP, bool RACE, int QPW>
 __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, const v4i *qop, float sq, int j,
                                           const uint8_t *cur, uint8_t *nxt, const int8_t *kg, const uint8_t *vg,
                                           const float *ksc, int wave, int lane, int row) {
@@ -161,7 +161,7 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   const int T = p.T;
   const int hi = lane >> 5;   // which 4-key group of each 8 this lane holds
   if (RACE) race_pause(p.race_seed, 0, j);
-  if (j + 1 < T) issue_tile<D>(nxt, kg, vg, j + 1, wave, lane);
+  if (j + 1 < T && (QPW == 1 || wave < 4)) issue_tile<D>(nxt, kg, vg, j + 1, wave, lane);
   const uint8_t *kl = cur + lane * 16;        // this lane's 16 bytes of every 1 KiB operand block
   const uint8_t *vl = kl + TILE;
 
@@ -310,8 +310,13 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   __syncthreads();
 }
 
-template <int D, bool CAP, bool RACE>
-__global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_fwd(FwdParams p) {
+// QPW: 128-row Q blocks per workgroup.  1 is the default schedule; 3 is the
+// paired schedule (the analogue of temporal pairing, "Experiment Log", Closed
+// Prior Work, and the split variants of the Phase 1 decision): three Q blocks
+// of one (b,h), twelve waves, share one K/V tile stream through LDS, so each
+// K/V tile is copied from L2 once per three blocks instead of once per block.
+template <int D, bool CAP, bool RACE, int QPW>
+__global__ __launch_bounds__(256 * QPW, FwdOccupancy<D>::waves_per_simd) void k_attn_fwd(FwdParams p) {
   constexpr int NS = D / 32;                 // INT8 k-steps per key row == PV row blocks
   constexpr int TILE = kBK * D;              // bytes of one K (or V) tile
   // two LDS buffers of [K tile | V tile], alternating per tile
@@ -321,12 +326,19 @@ __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_f
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index as a scalar: tile-copy addresses and LDS bases stay in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int u;
+  int u, wq = wave;           // work unit of this wave, wave index inside its Q block
+  bool live = true;           // false: a wave group past the head's last Q block (paired schedule)
   if (CAP) {
     u = p.units[blockIdx.x];
     if (u < 0 || u >= p.n_units) return;
-  } else {
+  } else if (QPW == 1) {
     u = xcd_remap(blockIdx.x, gridDim.x);
+  } else {
+    const int g = xcd_remap(blockIdx.x, gridDim.x), ngq = (p.nqb + QPW - 1) / QPW;
+    const int gbh = g / ngq, qraw = (g - gbh * ngq) * QPW + wave / 4;
+    live = qraw < p.nqb;
+    u = gbh * p.nqb + (live ? qraw : p.nqb - 1);   // a dead group repeats the last block, stores nothing
+    wq = wave & 3;
   }
   const int bh = u / p.nqb, qb = u - bh * p.nqb;
   const int T = p.T;
@@ -335,17 +347,17 @@ __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_f
   const float *ksc = p.k_scale + (size_t)bh * T;
 
   if (RACE) race_pause(p.race_seed, 3, 0);
-  issue_tile<D>(lds_a, kg, vg, 0, wave, lane);
+  if (QPW == 1 || wave < 4) issue_tile<D>(lds_a, kg, vg, 0, wave, lane);
 
   // Q^T operand (B of the INT8 product) for this wave's 32 rows, kept in registers.
   v4i qop[NS];
   {
-    const int8_t *qsrc = p.q_codes + ((size_t)u * 4 + wave) * (NS * 1024) + lane * 16;
+    const int8_t *qsrc = p.q_codes + ((size_t)u * 4 + wq) * (NS * 1024) + lane * 16;
 #pragma unroll
     for (int s = 0; s < NS; ++s) qop[s] = *(const v4i *)(qsrc + s * 1024);
   }
   const float sq = load_uniform(p.q_scale + u);
-  const int row = wave * 32 + (lane & 31);
+  const int row = wq * 32 + (lane & 31);
 
   FwdState<D> st;
   st.m = -INFINITY;
@@ -361,7 +373,7 @@ __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_f
   for (int j = 0; j < T; ++j) {
     uint8_t *cur = (j & 1) ? lds_b : lds_a;
     uint8_t *nxt = (j & 1) ? lds_a : lds_b;
-    tile_step<D, CAP, RACE>(p, st, qop, sq, j, cur, nxt, kg, vg, ksc, wave, lane, row);
+    tile_step<D, CAP, RACE, QPW>(p, st, qop, sq, j, cur, nxt, kg, vg, ksc, wave, lane, row);
   }
 
   __builtin_amdgcn_s_setprio(3);                 // finish and free the slot quickly
@@ -371,10 +383,10 @@ __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_f
   // holds them through the traversal
   const int elane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int hi = elane >> 5;
-  const int n = qb * kBQ + wave * 32 + (elane & 31);
+  const int n = qb * kBQ + wq * 32 + (elane & 31);
   const float r = 1.0f / st.dsum;                 // "reciprocal" (d includes the 448)
-  if (CAP && hi == 0) p.r_cap[(size_t)blockIdx.x * kBQ + wave * 32 + (elane & 31)] = r;
-  if (n < p.Nq) {
+  if (CAP && hi == 0) p.r_cap[(size_t)blockIdx.x * kBQ + wq * 32 + (elane & 31)] = r;
+  if (live && n < p.Nq) {
     const int b = bh / p.H, h = bh - b * p.H;
     uint16_t *orow = p.out + b * p.os[0] + h * p.os[1] + (int64_t)n * p.os[2];
     const float *vs = p.v_scale + (size_t)bh * D;
@@ -396,16 +408,24 @@ __global__ __launch_bounds__(256, FwdOccupancy<D>::waves_per_simd) void k_attn_f
   }
 }
 
-hipError_t launch_fwd(const FwdParams &p, int D, int grid, bool capture, bool race, hipStream_t st) {
-  if (D == 128) {
-    if (capture) hipLaunchKernelGGL((k_attn_fwd<128, true, false>), dim3(grid), dim3(256), 0, st, p);
-    else if (race) hipLaunchKernelGGL((k_attn_fwd<128, false, true>), dim3(grid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((k_attn_fwd<128, false, false>), dim3(grid), dim3(256), 0, st, p);
+template <int D>
+static void launch_fwd_d(const FwdParams &p, int grid, bool capture, bool race, bool paired, hipStream_t st) {
+  if (capture) {
+    hipLaunchKernelGGL((k_attn_fwd<D, true, false, 1>), dim3(grid), dim3(256), 0, st, p);
+  } else if (race) {
+    hipLaunchKernelGGL((k_attn_fwd<D, false, true, 1>), dim3(grid), dim3(256), 0, st, p);
+  } else if (paired) {
+    const int groups = (p.n_units / p.nqb) * ((p.nqb + kPairedBlocks - 1) / kPairedBlocks);
+    hipLaunchKernelGGL((k_attn_fwd<D, false, false, kPairedBlocks>), dim3(groups), dim3(256 * kPairedBlocks), 0,
+                       st, p);
   } else {
-    if (capture) hipLaunchKernelGGL((k_attn_fwd<64, true, false>), dim3(grid), dim3(256), 0, st, p);
-    else if (race) hipLaunchKernelGGL((k_attn_fwd<64, false, true>), dim3(grid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((k_attn_fwd<64, false, false>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_attn_fwd<D, false, false, 1>), dim3(grid), dim3(256), 0, st, p);
   }
+}
+
+hipError_t launch_fwd(const FwdParams &p, int D, int grid, bool capture, bool race, bool paired, hipStream_t st) {
+  if (D == 128) launch_fwd_d<128>(p, grid, capture, race, paired, st);
+  else launch_fwd_d<64>(p, grid, capture, race, paired, st);
   return hipGetLastError();
 }
 

@@ -65,15 +65,18 @@ def lib() -> ctypes.CDLL:
         for name in ("sage_quant_prep", "sage_quant_prep_single_pass"):
             getattr(L, name).argtypes = [vp, vp, vp, ctypes.POINTER(SageShape), ctypes.POINTER(SageStrides),
                                          ctypes.POINTER(SageQuantC), vp]
-        L.sage_attn_fwd.argtypes = [ctypes.POINTER(SageQuantC), ctypes.POINTER(SageShape), f32, vp,
-                                    ctypes.POINTER(SageStrides), vp]
+        for name in ("sage_attn_fwd", "sage_attn_fwd_paired"):
+            getattr(L, name).argtypes = [ctypes.POINTER(SageQuantC), ctypes.POINTER(SageShape), f32, vp,
+                                         ctypes.POINTER(SageStrides), vp]
         L.sage_attn_fwd_capture.argtypes = [ctypes.POINTER(SageQuantC), ctypes.POINTER(SageShape), f32, vp,
                                             ctypes.POINTER(SageStrides), vp, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.sage_clock_sample.argtypes = [vp, vp]
         L.sage_device_check.argtypes = [ctypes.c_int]
         L.sage_status_string.argtypes = [ctypes.c_int]
         L.sage_status_string.restype = ctypes.c_char_p
         for name in ("sage_buffer_bytes", "sage_prep_status_offset", "sage_quant_prep",
-                     "sage_quant_prep_single_pass", "sage_attn_fwd", "sage_attn_fwd_capture", "sage_device_check"):
+                     "sage_quant_prep_single_pass", "sage_attn_fwd", "sage_attn_fwd_paired", "sage_attn_fwd_capture",
+                     "sage_device_check", "sage_clock_sample"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -216,15 +219,19 @@ def _out_tensor(quant: SageQuant, out):
 
 
 def sage_attn_fwd(quant: SageQuant, sm_scale: float | None = None, out: torch.Tensor | None = None,
-                  stream=None) -> torch.Tensor:
-    """Fused INT8-QK / FP8-PV online-softmax attention; returns bf16 [B,H,Nq,D]."""
+                  stream=None, paired: bool = False) -> torch.Tensor:
+    """Fused INT8-QK / FP8-PV online-softmax attention; returns bf16 [B,H,Nq,D].
+
+    paired selects sage_attn_fwd_paired (three Q blocks per workgroup share
+    one K/V stream; same results)."""
     out = _out_tensor(quant, out)
     st = SageStrides()
     st.o = _strides3(out)
     qc = quant.c_struct()
-    _check(lib().sage_attn_fwd(ctypes.byref(qc), ctypes.byref(quant.shape),
-                               ctypes.c_float(0.0 if sm_scale is None else sm_scale), out.data_ptr(),
-                               ctypes.byref(st), _stream_handle(stream, out.device)), "sage_attn_fwd")
+    name = "sage_attn_fwd_paired" if paired else "sage_attn_fwd"
+    _check(getattr(lib(), name)(ctypes.byref(qc), ctypes.byref(quant.shape),
+                                ctypes.c_float(0.0 if sm_scale is None else sm_scale), out.data_ptr(),
+                                ctypes.byref(st), _stream_handle(stream, out.device)), name)
     return out
 
 
@@ -264,3 +271,15 @@ def sage_attn_fwd_capture(quant: SageQuant, units, sm_scale: float | None = None
 def sage_attention(q, k, v, sm_scale: float | None = None) -> torch.Tensor:
     """Both calls of the hot path: prep then fused forward."""
     return sage_attn_fwd(sage_quant_prep(q, k, v), sm_scale)
+
+
+CLOCK_SAMPLES = 2048
+
+
+def sage_clock_sample(dst: torch.Tensor, stream=None) -> None:
+    """Record per-workgroup (shader-clock counter, 100 MHz counter, XCD id,
+    unit hardware id) into dst (int64 [CLOCK_SAMPLES, 4] on the GPU) when the
+    stream reaches this point."""
+    if dst.dtype != torch.int64 or dst.numel() < 4 * CLOCK_SAMPLES or not dst.is_cuda or not dst.is_contiguous():
+        raise ValueError("dst must be a contiguous int64 CUDA tensor of %d elements" % (4 * CLOCK_SAMPLES))
+    _check(lib().sage_clock_sample(dst.data_ptr(), _stream_handle(stream, dst.device)), "sage_clock_sample")

@@ -104,12 +104,13 @@ def test_prep_validation_before_any_hip_call(L, entry):
     assert call(q, k, v, ctypes.byref(d96), ctypes.byref(st), ctypes.byref(qc), None) == -3
 
 
-def test_fwd_validation_before_any_hip_call(L):
+@pytest.mark.parametrize("entry", ["sage_attn_fwd", "sage_attn_fwd_paired"])
+def test_fwd_validation_before_any_hip_call(L, entry):
     shape = sage.SageShape(2, 2, 300, 77, 128)
     st = _strides(2, 2, 300, 128)
     qc = _fake_quant()
     out = 1 << 36
-    f = L.sage_attn_fwd
+    f = getattr(L, entry)
     assert f(None, ctypes.byref(shape), 0.0, out, ctypes.byref(st), None) == -1
     assert f(ctypes.byref(qc), ctypes.byref(shape), 0.0, None, ctypes.byref(st), None) == -1
     assert f(ctypes.byref(qc), ctypes.byref(shape), 0.0, out + 8, ctypes.byref(st), None) == -4

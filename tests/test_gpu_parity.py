@@ -69,7 +69,7 @@ def _bits32(x):
 class Run:
     """One prep + fwd (+ capture of sampled units) on the GPU, plus host copies."""
 
-    def __init__(self, q, k, v, units, sm_scale=None, strided=False, single_pass=False):
+    def __init__(self, q, k, v, units, sm_scale=None, strided=False, single_pass=False, paired=False):
         self.q, self.k, self.v = q, k, v
         self.B, self.H, self.Nq, self.D = q.shape
         self.Nkv = k.shape[2]
@@ -81,10 +81,10 @@ class Run:
             vd = v.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
         else:
             qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-        print("  gpu run B=%d H=%d Nq=%d Nkv=%d D=%d units=%d strided=%s single_pass=%s"
-              % (self.B, self.H, self.Nq, self.Nkv, self.D, len(units), strided, single_pass), flush=True)
+        print("  gpu run B=%d H=%d Nq=%d Nkv=%d D=%d units=%d strided=%s single_pass=%s paired=%s"
+              % (self.B, self.H, self.Nq, self.Nkv, self.D, len(units), strided, single_pass, paired), flush=True)
         self.quant = sage.sage_quant_prep(qd, kd, vd, single_pass=single_pass)
-        self.out = sage.sage_attn_fwd(self.quant, sm_scale)
+        self.out = sage.sage_attn_fwd(self.quant, sm_scale, paired=paired)
         self.units = list(units)
         oc, caps = sage.sage_attn_fwd_capture(self.quant, self.units, sm_scale)
         torch.cuda.synchronize()
@@ -591,3 +591,36 @@ def test_sage_attention_close_to_exact_attention():
     cos = torch.nn.functional.cosine_similarity(o.flatten(), ref.flatten(), dim=0).item()
     print("  cosine vs fp32 attention: %.6f" % cos, flush=True)
     assert cos >= 0.999
+
+
+@pytest.mark.parametrize("Nq,Nkv,D", [(1000, 1000, 128), (100, 700, 64), (300, 129, 128), (520, 2000, 64)])
+def test_paired_forward_all_rows(Nq, Nkv, D):
+    """The paired schedule (three Q blocks per workgroup, one K/V stream) on
+    every row against the oracle; 1, 3, 5 and 8 Q blocks per head, so groups
+    with one or two Q blocks past the head's end occur.  Its output must also
+    equal the one-block kernel's (capture build) on every unit."""
+    q, k, v = make_inputs(WORKLOADS["ragged_tails"], seed=40 + Nq, B=1, H=3, Nq=Nq, Nkv=Nkv, D=D)
+    nqb = -(-Nq // 128)
+    run = Run(q, k, v, list(range(3 * nqb)), paired=True)
+    preps = {bh: run.oracle_prep(bh) for bh in range(3)}
+    for bh, p in preps.items():
+        check_prep_bh(run, bh, p)
+    stats = OStats()
+    check_units(run, stats, preps)
+    stats.check()
+
+
+def test_paired_forward_full_size_bit_identical():
+    """The paired schedule gives the default forward's bytes on the three
+    full-size workloads."""
+    dev = torch.device("cuda:0")
+    for name in ("dit_block", "long_video", "headdim64"):
+        q, k, v = make_inputs(WORKLOADS[name])
+        print("  paired vs default forward:", name, tuple(q.shape), flush=True)
+        quant = sage.sage_quant_prep(q.to(dev), k.to(dev), v.to(dev))
+        a = sage.sage_attn_fwd(quant)
+        b = sage.sage_attn_fwd(quant, paired=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+        del quant, a, b
+        torch.cuda.empty_cache()
