@@ -305,6 +305,9 @@ def main():
             sp_ms.append((a, b))
     torch.cuda.synchronize()
     res["prep_single_pass_ms_p50"] = statistics.median(a.elapsed_time(b) for a, b in sp_ms)
+    # status word of the last single-pass call: 0 unless a workgroup stopped
+    # waiting for its head's statistics (its outputs would then be invalid)
+    res["prep_single_pass_status"] = quant.single_pass_status()
     # The paired forward schedule (three Q blocks per workgroup share one K/V
     # stream; same output), timed apart from the step.
     pf_ms = []

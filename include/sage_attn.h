@@ -158,9 +158,10 @@ int sage_quant_prep(const void *q, const void *k, const void *v, const sage_shap
  * concurrently (other streams) with another single-pass prep or with kernels
  * that hold compute units indefinitely.  The wait is bounded (~0.1 s); one that
  * ran out leaves a nonzero status word in the workspace (at
- * sage_prep_status_offset) and the outputs of that call are invalid (never
- * observed in the tests, which check the word).  About
- * as fast as sage_quant_prep on the shapes measured so far.
+ * sage_prep_status_offset) and NaN K scales for the tiles of the workgroup
+ * that stopped waiting, so a forward on those buffers gives NaN rows instead of
+ * silently wrong ones (never observed; the tests and bench.py check the word).
+ * About as fast as sage_quant_prep on the shapes measured so far.
  */
 int sage_quant_prep_single_pass(const void *q, const void *k, const void *v, const sage_shape_t *shape,
                                 const sage_strides_t *strides, const sage_quant_t *quant, void *stream);
@@ -206,6 +207,8 @@ int sage_quant_prep_no_alloc(const void *q, const void *k, const void *v, const 
  */
 int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *shape, float sm_scale, void *out,
                   const sage_strides_t *strides, void *stream);
+/* (The forward reads every buffer of `quant` but the workspace, which may be
+ * NULL here; this holds for every forward entry below.) */
 
 /*
  * sage_attn_fwd with the paired schedule (the analogue of the pages' temporal

@@ -164,7 +164,7 @@ int fill_fwd(const sage_quant_t *q, const sage_shape_t *s, float sm_scale, void 
   int r = check_shape(s);
   if (r) return r;
   if (!out || !st) return SAGE_E_NULL;
-  if ((r = check_quant(q))) return r;
+  if ((r = check_quant(q, false))) return r;      // the forward does not use the workspace
   if (!aligned16(out) || check_strides(st->o)) return SAGE_E_ALIGN;
   if (!std::isfinite(sm_scale)) return SAGE_E_ARG;
   if (!rows_disjoint(s, st->o, s->Nq) || overlaps_quant(out, span_bytes(s, st->o, s->Nq), q, s))

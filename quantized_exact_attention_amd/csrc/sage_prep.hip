@@ -341,6 +341,7 @@ struct FusedSmem {
   } u;
   float red[kFusedRows(D) / kBK][4];
   int last;
+  int expired;                    // this group's wait for the head's statistics ran out
 };
 
 template <int D>
@@ -412,11 +413,19 @@ __device__ __forceinline__ void fused_kv_group(const PrepParams &p, int bh, int 
     completed_barrier();
     if (tid == 0) __hip_atomic_store(ready, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // Ordering: the head's statistics were written with agent-scope (coherent)
+  // stores that had completed before the flag was stored, and the loads below
+  // are coherent too and are issued only after the flag load has returned, so
+  // they observe those stores.  (Acquire/release fences would add L2
+  // write-back and invalidation on every workgroup, which measured 120 us on
+  // the long video workload.)
   if (tid == 0) {
     unsigned it = 0;
+    sm.expired = 0;
     while (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
       if (++it > kSpinLimit) {
         __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.expired = 1;
         break;
       }
       __builtin_amdgcn_s_sleep(8);
@@ -463,7 +472,9 @@ __device__ __forceinline__ void fused_kv_group(const PrepParams &p, int bh, int 
     if (j >= p.T) break;
     const float amax = fmaxf(fmaxf(sm.red[q][0], sm.red[q][1]), fmaxf(sm.red[q][2], sm.red[q][3]));
     const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-    if (tid == 0) p.k_scale[(size_t)bh * p.T + j] = amax > 0.f ? amax / 127.0f : 0.f;
+    // a group whose wait ran out writes NaN scales for its tiles: every output
+    // row of the head then comes out NaN instead of silently wrong
+    if (tid == 0) p.k_scale[(size_t)bh * p.T + j] = sm.expired ? __builtin_nanf("") : amax > 0.f ? amax / 127.0f : 0.f;
     int8_t *kdst = p.k_codes + ((size_t)bh * p.T + j) * kBK * D;
 #pragma unroll
     for (int i = q * RPTT; i < (q + 1) * RPTT; ++i) {

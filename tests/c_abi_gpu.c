@@ -90,6 +90,17 @@ int main(int argc, char **argv) {
     return 1;
   }
   HIP_OK(hipDeviceSynchronize());
+  if (single_pass) {
+    /* the single pass reports a workgroup that stopped waiting in its status word */
+    size_t off = 0;
+    uint32_t status = 1;
+    if ((r = sage_prep_status_offset(&s, &off)) != SAGE_OK) return 1;
+    HIP_OK(hipMemcpy(&status, (char *)quant.workspace + off, sizeof status, hipMemcpyDeviceToHost));
+    if (status != 0) {
+      fprintf(stderr, "single-pass prep status word %u\n", status);
+      return 1;
+    }
+  }
   HIP_OK(hipMemcpy(ho, dout, bq, hipMemcpyDeviceToHost));
   FILE *f = fopen(argv[9], "wb");
   if (!f || fwrite(ho, 1, bq, f) != bq) return 1;

@@ -131,6 +131,10 @@ def test_fwd_validation_before_any_hip_call(L, entry):
     nulls = _fake_quant()
     nulls.v_scale = None
     assert f(ctypes.byref(nulls), ctypes.byref(shape), 0.0, out, ctypes.byref(st), None) == -1
+    # the forward does not read the workspace, so a NULL one passes validation
+    no_ws = _fake_quant()
+    no_ws.workspace = None
+    assert f(ctypes.byref(no_ws), ctypes.byref(shape), 0.0, out, ctypes.byref(st), None) in (0, -6, -7)
     cap = L.sage_attn_fwd_capture
     caps = [1 << 37, 1 << 38, 1 << 39, 1 << 40, 1 << 41, 1 << 42]
     assert cap(ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(st), None, 1, *caps, None) == -1

@@ -29,6 +29,17 @@ def _no_alloc_prep(qd, kd, vd, quant):
                                                stream)
 
 
+def _no_workspace_fwd(quant, out):
+    """sage_attn_fwd through the C ABI with a NULL workspace (the forward does
+    not use it)."""
+    st = sage.SageStrides()
+    st.o = sage._strides3(out)
+    qc = quant.c_struct()
+    qc.workspace = None
+    return sage.lib().sage_attn_fwd(ctypes.byref(qc), ctypes.byref(quant.shape), ctypes.c_float(0.0),
+                                    out.data_ptr(), ctypes.byref(st), sage._stream_handle(None, out.device))
+
+
 def test_no_alloc_prep_matches_workspace_prep():
     dev = torch.device("cuda:0")
     lib = sage.lib()
@@ -55,7 +66,8 @@ def test_no_alloc_prep_matches_workspace_prep():
         for f in FIELDS:
             assert torch.equal(getattr(ref, f).view(torch.uint8), getattr(got, f).view(torch.uint8)), (name, f)
         o_ref = sage.sage_attn_fwd(ref)
-        o_got = sage.sage_attn_fwd(got)
+        o_got = torch.empty_like(o_ref)
+        assert _no_workspace_fwd(got, o_got) == 0         # the whole path without any workspace
         torch.cuda.synchronize()
         assert torch.equal(o_ref.view(torch.int16), o_got.view(torch.int16)), name
         del ref, got, qd, kd, vd, o_ref, o_got
