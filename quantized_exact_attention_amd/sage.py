@@ -11,8 +11,9 @@ Names mirror the C ABI in ``include/sage_attn.h``.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 
 import torch
 
@@ -91,6 +92,7 @@ def status_string(status: int) -> str:
     return lib().sage_status_string(status).decode()
 
 
+@functools.lru_cache(maxsize=256)
 def sage_buffer_bytes(B: int, H: int, Nq: int, Nkv: int, D: int, which: int) -> int:
     n = ctypes.c_size_t(0)
     shape = SageShape(B, H, Nq, Nkv, D)
@@ -127,6 +129,9 @@ class SageQuant:
     v_scale: torch.Tensor
     k_mean: torch.Tensor
     workspace: torch.Tensor
+    # (buffer addresses and sizes, device) last validated, and its C struct
+    _checked: tuple = field(default=None, repr=False, compare=False)
+    _cstruct: object = field(default=None, repr=False, compare=False)
 
     @property
     def shape(self) -> SageShape:
@@ -140,15 +145,27 @@ class SageQuant:
     def T(self) -> int:
         return -(-self.Nkv // BK)
 
+    def _key(self, device):
+        bufs = [getattr(self, n) for n in BUFFERS]
+        if not all(isinstance(t, torch.Tensor) for t in bufs):
+            return None
+        return (device,) + tuple((t.data_ptr(), t.numel(), t.is_contiguous(), t.device) for t in bufs)
+
     def check_buffers(self, device: torch.device):
         """Every buffer on `device`, contiguous and at least as large as the C
-        ABI's size for this shape (a caller-built or reused set included)."""
+        ABI's size for this shape (a caller-built or reused set included).
+        The outcome is remembered for the same buffers, so repeated calls on
+        one set cost one address comparison."""
+        key = self._key(device)
+        if key is not None and key == self._checked:
+            return
         for i, name in enumerate(BUFFERS):
             t = getattr(self, name)
             if not isinstance(t, torch.Tensor) or t.device != device or not t.is_contiguous():
                 raise ValueError("quant.%s must be a contiguous tensor on %s" % (name, device))
             if t.numel() * t.element_size() < sage_buffer_bytes(self.B, self.H, self.Nq, self.Nkv, self.D, i):
                 raise ValueError("quant.%s is smaller than the shape needs" % name)
+        self._checked = key
 
     def single_pass_status(self) -> int:
         """Status word of the last single-pass prep into these buffers (0: every
@@ -160,7 +177,10 @@ class SageQuant:
         return int(self.workspace[off.value:off.value + 4].cpu().view(torch.int32).item())
 
     def c_struct(self) -> SageQuantC:
-        return SageQuantC(*[getattr(self, n).data_ptr() for n in BUFFERS])
+        ptrs = tuple(getattr(self, n).data_ptr() for n in BUFFERS)
+        if self._cstruct is None or self._cstruct[0] != ptrs:
+            self._cstruct = (ptrs, SageQuantC(*ptrs))
+        return self._cstruct[1]
 
     @classmethod
     def allocate(cls, B, H, Nq, Nkv, D, device) -> "SageQuant":
