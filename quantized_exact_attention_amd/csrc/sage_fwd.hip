@@ -4,9 +4,12 @@
 // Verification: QK traversal (INT8, int32 accumulation), online softmax, FP8
 // probabilities, two-level PV accumulation and final conversion, keeping the
 // invariants of the Phase 1 State-Ownership Decision (strict KV-tile order,
-// exact FP8 score bytes, per-tile RO rescaling, two-level PV) and producing the
-// checkpoints named in Phase 2B Fixed Aligned Numerical Prototype (QK, m, d,
-// FP8 probability, rescale, PV partial, RO, reciprocal, BF16 output).
+// exact FP8 score bytes, per-tile RO rescaling, two-level PV).  The capture
+// build (template flag CAP) writes, for listed work units, every checkpoint
+// named in Phase 2B Fixed Aligned Numerical Prototype (QK, m, d, FP8
+// probability, rescale, PV partial, RO, reciprocal, BF16 output); the race-gate
+// build (RACE) adds seeded pauses before every LDS access and tile copy; QPW
+// selects one Q block per workgroup (default) or the paired schedule.
 //
 // Work decomposition: one workgroup = 4 wavefronts = one 128-row Q block of one
 // (b,h); each wavefront owns 32 query rows and walks all 64-key tiles in order.
