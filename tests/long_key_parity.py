@@ -1,7 +1,7 @@
 """Tile indices past 65536 against the oracle: one head of 4.2M keys.
 
-Not collected by pytest (the oracle's prep of 4.2M keys takes minutes); run on
-a machine with the GPU:
+Not collected by pytest (about a minute of oracle time per head dimension,
+over the suite's per-test limit); run on a machine with the GPU:
 
     python tests/long_key_parity.py 128      # or 64
 
