@@ -28,6 +28,11 @@ pytestmark = pytest.mark.gpu
 
 O_MAX_ABS = 1e-2
 O_MEAN_REL = 1e-3
+# Entries over 1e-2 (allowed only by one bf16 unit at |O| >= 2, or a flipped P8
+# code's share) may be at most this fraction of a run's output entries; none on
+# the Gaussian workloads, whose |O| stays far below 2.
+O_OVER_FRAC = 1e-3
+O_OVER_FRAC_GAUSSIAN = 0.0
 P8_EQUAL_FRAC = 0.999
 # d (= sum of p, carried as 448*d on the GPU) differs by the rounding of the
 # exp2 argument at the running max (|m| reaches a few hundred with x20
@@ -182,7 +187,9 @@ class OStats:
         self.p8_equal += int((got == ref).sum())
         self.p8_maxdiff = max(self.p8_maxdiff, int(np.abs(got.astype(np.int64) - ref.astype(np.int64)).max(initial=0)))
 
-    def check(self):
+    def check(self, over_frac=O_OVER_FRAC):
+        """over_frac: budget for entries over 1e-2, as a fraction of the
+        entries checked (None: no budget, for runs chosen for such entries)."""
         mean_rel = self.sum_abs_diff / max(self.sum_abs_ref, 1e-300)
         print("  O max_abs=%.3g mean_rel=%.3g, %d of %d entries bit-equal; above 1e-2: %d (within one bf16"
               " unit, R20: %d; within a flipped P8 code's share, R21: %d; beyond both: %d); P8 equal %d/%d,"
@@ -197,6 +204,9 @@ class OStats:
                      self.r_max_rel), flush=True)
         assert self.n_bad == 0, "O entries beyond max(1e-2, 1 bf16 ulp): %d" % self.n_bad
         assert mean_rel <= O_MEAN_REL
+        if over_frac is not None:
+            assert self.n_over <= over_frac * self.n_o, "%d of %d entries over 1e-2 (budget %g)" % (
+                self.n_over, self.n_o, over_frac)
         if self.p8_total:
             assert self.p8_equal >= P8_EQUAL_FRAC * self.p8_total
             assert self.p8_maxdiff <= 1
@@ -313,7 +323,7 @@ def sample_units(nqb, BH, n_random, seed):
     return sorted(picks)
 
 
-def run_full(name, n_random=5, **over):
+def run_full(name, n_random=5, over_frac=O_OVER_FRAC, **over):
     w = WORKLOADS[name]
     q, k, v = make_inputs(w, **over)
     B, H, Nq, D = q.shape
@@ -327,7 +337,7 @@ def run_full(name, n_random=5, **over):
         check_prep_bh(run, bh, p)
     stats = OStats()
     check_units(run, stats, preps)
-    stats.check()
+    stats.check(over_frac)
     return run
 
 
@@ -341,7 +351,7 @@ def test_single_tile_all_rows():
     check_prep_bh(run, 0, p)
     stats = OStats()
     check_units(run, stats, {0: p})
-    stats.check()
+    stats.check(O_OVER_FRAC_GAUSSIAN)
 
 
 def sync_words(run):
@@ -381,11 +391,11 @@ def test_ragged_tails_all_rows(single_pass):
 
 
 def test_dit_block_full_size_sampled():
-    run_full("dit_block")
+    run_full("dit_block", over_frac=O_OVER_FRAC_GAUSSIAN)
 
 
 def test_long_video_full_size_sampled():
-    run_full("long_video", n_random=4)
+    run_full("long_video", n_random=4, over_frac=O_OVER_FRAC_GAUSSIAN)
 
 
 def test_headdim64_full_size_sampled():
