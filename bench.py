@@ -6,6 +6,9 @@ bf16 inputs already resident in HBM.  Prints ONE JSON line:
   roofline    the fused forward kernel against the dense INT8/FP8 matrix peak,
               timed with HIP events on the stream it is launched on
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
+  mfma_peak_measured  the matrix cores' sustained INT8 and FP8 rates on this
+              box (a pure matrix-instruction stream), with the forward's
+              rate against them
 Default workload: the long video-token sequence (B=1, H=24, N=32760, D=128).
 """
 
@@ -321,6 +324,31 @@ def main():
             pf_ms.append((a, b))
     torch.cuda.synchronize()
     res["fwd_paired_ms_p50"] = statistics.median(a.elapsed_time(b) for a, b in pf_ms)
+    # The matrix cores' sustained rate on this machine: a pure matrix-instruction
+    # stream on every SIMD (INT8 32x32x32, then FP8 32x32x64), median of three
+    # timed launches after a warm one, with the shader clock over them; the
+    # forward's rate against it (half of its operations are INT8, half FP8).
+    peak_dst = torch.empty(sage.PEAK_WORKGROUPS * 256, dtype=torch.int32, device=dev)
+    peak = {}
+    for kind, name in ((0, "int8"), (1, "fp8")):
+        sage.sage_mfma_peak_sample(kind, 1, peak_dst, stream)
+        torch.cuda.synchronize()
+        rates = []
+        sage.sage_clock_sample(clk[0], stream)
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            ops = sage.sage_mfma_peak_sample(kind, 4096, peak_dst, stream)
+            b.record(stream)
+            rates.append((a, b, ops))
+        sage.sage_clock_sample(clk[1], stream)
+        torch.cuda.synchronize()
+        peak[name + "_tops"] = statistics.median(ops / (a.elapsed_time(b) * 1e-3) / 1e12 for a, b, ops in rates)
+        sc = shader_clock_ghz(clk.cpu().numpy())
+        peak[name + "_sclk_ghz"] = sc["median"] if sc else None
+    peak["unit"] = "TOP/s"
+    peak["fwd_frac_of_measured"] = achieved / (0.5 * (peak["int8_tops"] + peak["fp8_tops"]))
+    res["mfma_peak_measured"] = peak
     if w.name == "single_tile":
         # the pages quote this fixture's forward both batched and as single
         # launches (2,000 samples); time single launches the same way: one

@@ -275,6 +275,22 @@ int sage_race_gate(const void *q, const void *k, const void *v, const sage_shape
 #define SAGE_CLOCK_SAMPLES 2048
 int sage_clock_sample(uint64_t *dst, void *stream);
 
+/* Diagnostics: a sample of the matrix cores' sustained rate, for comparing the
+ * forward with what the hardware reaches rather than only with the nominal
+ * peak.  SAGE_PEAK_WORKGROUPS workgroups of four waves (four waves per SIMD of
+ * a 256-CU device); every wave issues `iters` rounds of four independent
+ * accumulation chains of one matrix instruction on register operands:
+ * kind 0 = v_mfma_i32_32x32x32_i8 (32*32*32*2 = 65536 ops each), kind 1 =
+ * v_mfma_f32_32x32x64_f8f6f4 with E4M3 operands (131072 ops each).  Operations
+ * per call: SAGE_PEAK_WORKGROUPS * 4 * iters * 4 * (ops per instruction); the
+ * caller times the call with events on `stream`.  Each thread writes one word
+ * of its accumulators to dst[SAGE_PEAK_WORKGROUPS * 256] (device, 4-byte
+ * aligned; caller-owned; contents meaningless).  SAGE_E_ARG for a kind other
+ * than 0 or 1 or iters outside [1, SAGE_PEAK_MAX_ITERS]. */
+#define SAGE_PEAK_WORKGROUPS 1024
+#define SAGE_PEAK_MAX_ITERS 65536
+int sage_mfma_peak_sample(int kind, int iters, uint32_t *dst, void *stream);
+
 /* SAGE_OK if `device` is a gfx950 GPU, else SAGE_E_DEVICE (one HIP query). */
 int sage_device_check(int device);
 

@@ -203,9 +203,56 @@ __global__ void k_clock_sample(uint64_t *dst) {
   }
 }
 
+// Matrix-core peak sample: four independent accumulation chains of one
+// matrix instruction per wave on register operands, so that each SIMD's matrix
+// core is fed back to back (a dependent chain of one instruction would wait for
+// its own result).  The operands are fixed non-NaN bit patterns; the values
+// are irrelevant, the last lane words keep the work from being removed.
+template <int KIND>
+__global__ __launch_bounds__(256) void k_mfma_peak(int iters, uint32_t *dst) {
+  const int lane = threadIdx.x & 63;
+  uint32_t word;
+  if (KIND == 0) {
+    const v4i a = {lane, lane * 3, lane * 5, lane * 7}, b = {lane * 11, lane * 13, 17, 19};
+    v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int i = 0; i < iters; ++i) {
+      c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c3, 0, 0, 0);
+    }
+    word = (uint32_t)(c0[lane & 15] ^ c1[3] ^ c2[7] ^ c3[15]);
+  } else {
+    const int e = 0x38302820;   // E4M3 codes of 1.0, 0.5, 0.25, 0.125
+    const v8i a = {e, e, e, e, e, e, e, e}, b = {e, e, e, e, e, e, e, e};
+    v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int i = 0; i < iters; ++i) {
+      c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, 0, 0, 0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c1, 0, 0, 0, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c2, 0, 0, 0, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c3, 0, 0, 0, 0, 0, 0);
+    }
+    word = __float_as_uint(c0[lane & 15] + c1[3] + c2[7] + c3[15]);
+  }
+  dst[(size_t)blockIdx.x * 256 + threadIdx.x] = word;
+}
+
 }  // namespace
 
 extern "C" {
+
+int sage_mfma_peak_sample(int kind, int iters, uint32_t *dst, void *stream) {
+  if (!dst) return SAGE_E_NULL;
+  if (((uintptr_t)dst & 3u) != 0) return SAGE_E_ALIGN;
+  if ((kind != 0 && kind != 1) || iters < 1 || iters > SAGE_PEAK_MAX_ITERS) return SAGE_E_ARG;
+  int r = device_ok();
+  if (r) return r;
+  if (kind == 0)
+    hipLaunchKernelGGL(k_mfma_peak<0>, dim3(SAGE_PEAK_WORKGROUPS), dim3(256), 0, (hipStream_t)stream, iters, dst);
+  else
+    hipLaunchKernelGGL(k_mfma_peak<1>, dim3(SAGE_PEAK_WORKGROUPS), dim3(256), 0, (hipStream_t)stream, iters, dst);
+  return hipGetLastError() == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
+}
 
 int sage_clock_sample(uint64_t *dst, void *stream) {
   if (!dst) return SAGE_E_NULL;

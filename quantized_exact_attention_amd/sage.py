@@ -72,12 +72,13 @@ def lib() -> ctypes.CDLL:
         L.sage_attn_fwd_capture.argtypes = [ctypes.POINTER(SageQuantC), ctypes.POINTER(SageShape), f32, vp,
                                             ctypes.POINTER(SageStrides), vp, i32, vp, vp, vp, vp, vp, vp, vp]
         L.sage_clock_sample.argtypes = [vp, vp]
+        L.sage_mfma_peak_sample.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
         L.sage_device_check.argtypes = [ctypes.c_int]
         L.sage_status_string.argtypes = [ctypes.c_int]
         L.sage_status_string.restype = ctypes.c_char_p
         for name in ("sage_buffer_bytes", "sage_prep_status_offset", "sage_quant_prep",
                      "sage_quant_prep_single_pass", "sage_attn_fwd", "sage_attn_fwd_paired", "sage_attn_fwd_capture",
-                     "sage_device_check", "sage_clock_sample"):
+                     "sage_device_check", "sage_clock_sample", "sage_mfma_peak_sample"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -303,3 +304,20 @@ def sage_clock_sample(dst: torch.Tensor, stream=None) -> None:
     if dst.dtype != torch.int64 or dst.numel() < 4 * CLOCK_SAMPLES or not dst.is_cuda or not dst.is_contiguous():
         raise ValueError("dst must be a contiguous int64 CUDA tensor of %d elements" % (4 * CLOCK_SAMPLES))
     _check(lib().sage_clock_sample(dst.data_ptr(), _stream_handle(stream, dst.device)), "sage_clock_sample")
+
+
+PEAK_WORKGROUPS = 1024
+PEAK_MAX_ITERS = 65536
+PEAK_OPS_PER_INSTRUCTION = {0: 32 * 32 * 32 * 2, 1: 32 * 32 * 64 * 2}   # kind 0: INT8, kind 1: FP8
+
+
+def sage_mfma_peak_sample(kind: int, iters: int, dst: torch.Tensor, stream=None) -> int:
+    """Launch the matrix-core peak sample (kind 0: INT8 32x32x32, 1: FP8
+    32x32x64) on `stream`; dst: contiguous int32 CUDA tensor of
+    PEAK_WORKGROUPS * 256 elements (scratch).  Returns the number of operations
+    the launch performs; the caller times it."""
+    if dst.dtype != torch.int32 or dst.numel() < PEAK_WORKGROUPS * 256 or not dst.is_cuda or not dst.is_contiguous():
+        raise ValueError("dst must be a contiguous int32 CUDA tensor of %d elements" % (PEAK_WORKGROUPS * 256))
+    _check(lib().sage_mfma_peak_sample(kind, iters, dst.data_ptr(), _stream_handle(stream, dst.device)),
+           "sage_mfma_peak_sample")
+    return PEAK_WORKGROUPS * 4 * iters * 4 * PEAK_OPS_PER_INSTRUCTION[kind]

@@ -21,6 +21,15 @@ def L():
     return sage.lib()
 
 
+@pytest.fixture(scope="module")
+def no_gfx950(L):
+    """For tests whose calls pass validation with made-up device addresses:
+    they rely on the library stopping at its device check, so they must not run
+    where a gfx950 GPU would take the launch."""
+    if L.sage_device_check(0) == 0:
+        pytest.skip("a gfx950 device is present: made-up device addresses would reach a kernel")
+
+
 def header_functions():
     text = open(os.path.join(ROOT, "include", "sage_attn.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -105,7 +114,7 @@ def test_prep_validation_before_any_hip_call(L, entry):
 
 
 @pytest.mark.parametrize("entry", ["sage_attn_fwd", "sage_attn_fwd_paired"])
-def test_fwd_validation_before_any_hip_call(L, entry):
+def test_fwd_validation_before_any_hip_call(L, entry, no_gfx950):
     shape = sage.SageShape(2, 2, 300, 77, 128)
     st = _strides(2, 2, 300, 128)
     qc = _fake_quant()
@@ -157,7 +166,7 @@ def test_binding_fails_loudly_without_library(monkeypatch):
         sage.lib()
 
 
-def test_no_alloc_prep_rejects_shapes_beyond_its_scratch(L):
+def test_no_alloc_prep_rejects_shapes_beyond_its_scratch(L, no_gfx950):
     """The allocation-free prep checks its static 8 MiB scratch against the
     shape before any HIP call; a NULL workspace is accepted there."""
     f = L.sage_quant_prep_no_alloc
@@ -185,7 +194,7 @@ def test_no_alloc_prep_rejects_shapes_beyond_its_scratch(L):
              None) == -1
 
 
-def test_race_gate_validation_before_any_hip_call(L):
+def test_race_gate_validation_before_any_hip_call(L, no_gfx950):
     f = L.sage_race_gate
     f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.POINTER(sage.SageShape), ctypes.POINTER(sage.SageStrides),
                                           ctypes.POINTER(sage.SageQuantC), ctypes.c_float, ctypes.c_void_p,
@@ -199,3 +208,13 @@ def test_race_gate_validation_before_any_hip_call(L):
     assert f(q, k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(qc), 0.0, q, 5, None) == -5
     assert f(q, k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(qc), 0.0, None, 5, None) == -1
     assert f(q, k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(qc), 0.0, out, 5, None) in (-6, -7, 0)
+
+
+def test_mfma_peak_sample_validation_before_any_hip_call(L, no_gfx950):
+    f = L.sage_mfma_peak_sample
+    dst = 1 << 44
+    assert f(0, 16, None, None) == -1
+    assert f(0, 16, dst + 2, None) == -4
+    for kind, iters in ((2, 16), (-1, 16), (0, 0), (1, -5), (1, 65537)):
+        assert f(kind, iters, dst, None) == -8, (kind, iters)
+    assert f(1, 65536, dst, None) in (0, -6, -7)
