@@ -208,8 +208,9 @@ class OStats:
             assert self.n_over <= over_frac * self.n_o, "%d of %d entries over 1e-2 (budget %g)" % (
                 self.n_over, self.n_o, over_frac)
         if self.p8_total:
-            assert self.p8_equal >= P8_EQUAL_FRAC * self.p8_total
-            assert self.p8_maxdiff <= 1
+            assert self.p8_equal >= P8_EQUAL_FRAC * self.p8_total, "P8 codes equal on only %d of %d" % (
+                self.p8_equal, self.p8_total)
+            assert self.p8_maxdiff <= 1, "P8 code off by %d" % self.p8_maxdiff
 
 
 def p8_flip_allowance(p8_gpu, ck, p, nkv):
