@@ -7,7 +7,7 @@ bf16 inputs already resident in HBM.  Prints ONE JSON line:
               timed with HIP events on the stream it is launched on
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
   mfma_peak_measured  the matrix cores' sustained INT8 and FP8 rates on this
-              box (a pure matrix-instruction stream), with the forward's
+              device (a pure matrix-instruction stream), with the forward's
               rate against them
 Default workload: the long video-token sequence (B=1, H=24, N=32760, D=128).
 """
@@ -324,7 +324,7 @@ def main():
             pf_ms.append((a, b))
     torch.cuda.synchronize()
     res["fwd_paired_ms_p50"] = statistics.median(a.elapsed_time(b) for a, b in pf_ms)
-    # The matrix cores' sustained rate on this machine: a pure matrix-instruction
+    # The matrix cores' sustained rate on this device: a pure matrix-instruction
     # stream on every SIMD (INT8 32x32x32, then FP8 32x32x64), median of three
     # timed launches after a warm one, with the shader clock over them; the
     # forward's rate against it (half of its operations are INT8, half FP8).

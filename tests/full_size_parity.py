@@ -4,6 +4,7 @@ Not collected by pytest (the long video workload takes about four minutes of
 oracle time on 16 cores); run it on a machine with the GPU:
 
     python tests/full_size_parity.py dit_block      # or long_video, headdim64, ...
+    python tests/full_size_parity.py dit_block --summary PATH   # also append the summary line to PATH
 
 The oracle runs first, one (b,h) per task in up to 16 spawned single-threaded
 processes (before this process touches the GPU); then the library runs the
@@ -14,6 +15,8 @@ rows over that per-element bar are run again with checkpoint capture and
 judged as the parity tests judge them, with the share of any FP8 probability
 code that differs from the oracle's.
 """
+
+from __future__ import annotations
 
 import json
 import os
@@ -38,7 +41,7 @@ def _oracle_head(args):
     return p.k_mean, p.q_scale, p.k_scale, p.v_scale, p.q_codes, p.k_codes, p.v_codes, O
 
 
-def main(workload: str, procs: int) -> None:
+def main(workload: str, procs: int, summary_path: str | None = None) -> None:
     import multiprocessing as mp
     from concurrent.futures import ProcessPoolExecutor
 
@@ -99,9 +102,10 @@ def main(workload: str, procs: int) -> None:
                "bit_equal": stats.n_equal, "max_abs": stats.max_abs, "mean_rel": mean_rel,
                "over_1e-2": stats.n_over, "pass_by_R20": stats.n_r20, "pass_by_R21": n_r21,
                "kernel_source_hash": kernel_source_hash()}
-    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
-    with open(os.path.join(ROOT, "gpurun_out", "full_size_parity.jsonl"), "a") as fh:
-        fh.write(json.dumps(summary) + "\n")
+    if summary_path:
+        os.makedirs(os.path.dirname(os.path.abspath(summary_path)), exist_ok=True)
+        with open(summary_path, "a") as fh:
+            fh.write(json.dumps(summary) + "\n")
     print("full-size parity: %s, %d heads, %d units: OK %s" % (workload, len(heads), len(heads) * nqb,
                                                               json.dumps(summary)), flush=True)
 
@@ -117,5 +121,9 @@ def kernel_source_hash() -> str:
 
 
 if __name__ == "__main__":
-    main(sys.argv[1] if len(sys.argv) > 1 else "dit_block",
-         int(os.environ.get("ORACLE_PROCS", min(16, len(os.sched_getaffinity(0))))))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("workload", nargs="?", default="dit_block")
+    ap.add_argument("--summary", default=None, help="append the JSON summary line to this file")
+    a = ap.parse_args()
+    main(a.workload, int(os.environ.get("ORACLE_PROCS", min(16, len(os.sched_getaffinity(0))))), a.summary)

@@ -13,9 +13,11 @@ change the output completely), K rounded to multiples of 2^-12 so that its
 column sums are exact in float64.  The library runs prep and forward once.
 Checked against the oracle: K mean, every scale and every Q, K and V code
 bit-exact; the output on every one of the 130 rows within max(1e-2, one bf16
-unit) per element and mean-rel <= 1e-3.  Appends a summary line to
-gpurun_out/long_key_parity.jsonl.
+unit) per element and mean-rel <= 1e-3.  With --summary PATH, appends the
+summary line to PATH.
 """
+
+from __future__ import annotations
 
 import json
 import os
@@ -29,7 +31,7 @@ if ROOT not in sys.path:
 import numpy as np  # noqa: E402
 
 
-def main(D: int) -> None:
+def main(D: int, summary_path: str | None = None) -> None:
     import torch
 
     from oracle import sage_oracle as so
@@ -83,11 +85,17 @@ def main(D: int) -> None:
     summary = {"D": D, "Nq": Nq, "Nkv": Nkv, "tiles": -(-Nkv // 64), "entries": stats.n_o, "bit_equal": stats.n_equal,
                "max_abs": stats.max_abs, "mean_rel": stats.sum_abs_diff / stats.sum_abs_ref,
                "over_1e-2": stats.n_over, "pass_by_R20": stats.n_r20}
-    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
-    with open(os.path.join(ROOT, "gpurun_out", "long_key_parity.jsonl"), "a") as fh:
-        fh.write(json.dumps(summary) + "\n")
+    if summary_path:
+        os.makedirs(os.path.dirname(os.path.abspath(summary_path)), exist_ok=True)
+        with open(summary_path, "a") as fh:
+            fh.write(json.dumps(summary) + "\n")
     print("long-key parity OK", json.dumps(summary), flush=True)
 
 
 if __name__ == "__main__":
-    main(int(sys.argv[1]) if len(sys.argv) > 1 else 128)
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("D", nargs="?", type=int, default=128)
+    ap.add_argument("--summary", default=None, help="append the JSON summary line to this file")
+    a = ap.parse_args()
+    main(a.D, a.summary)

@@ -1,14 +1,14 @@
-"""The GPU parity checker, tested on the CPU with planted mistakes.
+"""The GPU parity comparison, tested on the CPU with planted mistakes.
 
-The checker of tests/test_gpu_parity.py compares the library's buffers with
-the oracle.  Here a stand-in for those buffers is built from the oracle's own
-results (in the library's layouts where the checker reads them), so the
-unmodified stand-in must pass every check; then one mistake at a time is
-planted in the stand-in (one code, one scale, one score, one checkpoint, one
-output entry) and the checker must fail, naming the stage.  This is the host
-fault-injection tier of the test plan, done without a GPU: the repetition test
-of "Experiment Log", Phase 2B, found a slot-indexing bug that way on the pages'
-machine, and the checker must be able to see such a mistake at every stage.
+The comparison functions of tests/test_gpu_parity.py hold the library's
+buffers against the oracle.  Here a stand-in for those buffers is built from
+the oracle's own results (in the library's layouts where the comparison reads
+them), so the unmodified stand-in must pass every check; then one mistake at a
+time is planted in the stand-in (one code, one scale, one score, one
+checkpoint, one output entry) and the comparison must fail, naming the stage.
+This is host fault injection done without a GPU: the repetition test of
+"Experiment Log", Phase 2B, found a slot-indexing bug on the pages' machine,
+and the comparison must be able to see such a mistake at every stage.
 """
 
 import copy
@@ -29,7 +29,7 @@ class _Quant:
 
 
 class OracleStandIn:
-    """The attributes of tests/test_gpu_parity.Run that the checker reads,
+    """The attributes of tests/test_gpu_parity.Run that the comparison reads,
     filled from the oracle: prep outputs, the forward's output bits and the
     capture buffers of every unit (rows padded to 128, keys to T*64)."""
 
@@ -94,7 +94,7 @@ def _check_all(run):
     stats.check(tp.O_OVER_FRAC_GAUSSIAN)
 
 
-def test_checker_accepts_the_oracle_itself(clean):
+def test_comparison_accepts_the_oracle_itself(clean):
     _check_all(clean)
 
 
@@ -154,14 +154,14 @@ def _plant(clean, what):
                                   "S mismatch", "m mismatch", "d mismatch", "alpha", "partial, tile",
                                   "RO, tile", "reciprocal", "capture O != fast O", "O entries beyond",
                                   "masked P8 not zero"])
-def test_checker_names_the_planted_stage(clean, what):
+def test_comparison_names_the_planted_stage(clean, what):
     run = _plant(clean, what)
     with pytest.raises(AssertionError) as e:
         _check_all(run)
-    assert what in str(e.value), "planted %r, checker said %r" % (what, str(e.value)[:200])
+    assert what in str(e.value), "planted %r, comparison said %r" % (what, str(e.value)[:200])
 
 
-def test_checker_rejects_a_probability_code_two_steps_off(clean):
+def test_comparison_rejects_a_probability_code_two_steps_off(clean):
     """P8 may differ by one code at a rounding near-tie, never by two."""
     run = _plant(clean, "P8 two codes")
     with pytest.raises(AssertionError) as e:
