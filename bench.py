@@ -324,6 +324,32 @@ def main():
             pf_ms.append((a, b))
     torch.cuda.synchronize()
     res["fwd_paired_ms_p50"] = statistics.median(a.elapsed_time(b) for a, b in pf_ms)
+    # The Q-quantizing pair (sage_quant_prep_kv + sage_attn_fwd_q: the Q codes
+    # never pass through memory; bit-identical output), timed as a step apart
+    # from the headline one.
+    kv = sage.sage_quant_prep_kv(kd, vd)
+    out_q = sage.sage_attn_fwd_q(qd, kv)
+    torch.cuda.synchronize()
+    fq = []
+    for i in range(args.warmup + args.steps):
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        sage.sage_quant_prep_kv(kd, vd, out=kv)
+        b.record(stream)
+        sage.sage_attn_fwd_q(qd, kv, out=out_q)
+        c.record(stream)
+        if i >= args.warmup:
+            fq.append((a, b, c))
+    torch.cuda.synchronize()
+    fq_step = statistics.median(a.elapsed_time(c) for a, b, c in fq)
+    res["q_quantizing_pair"] = {
+        "step_ms_p50": fq_step,
+        "tflops_p50": w.flops / (fq_step * 1e-3) / 1e12,
+        "prep_kv_ms_p50": statistics.median(a.elapsed_time(b) for a, b, c in fq),
+        "fwd_q_ms_p50": statistics.median(b.elapsed_time(c) for a, b, c in fq),
+        "output_equal": bool(torch.equal(out_q.view(torch.int16), out.view(torch.int16))),
+    }
+    del kv, out_q
     # The matrix cores' sustained rate on this device: a pure matrix-instruction
     # stream on every SIMD (INT8 32x32x32, then FP8 32x32x64), median of three
     # timed launches after a warm one, with the shader clock over them; the

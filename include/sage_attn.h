@@ -211,6 +211,37 @@ int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *shape, float sm
  * NULL here; this holds for every forward entry below.) */
 
 /*
+ * K/V half of sage_quant_prep: the K mean, K smoothing and per-tile INT8 K, and
+ * the per-channel FP8 V of stage 1-2 above ("Experiment Log", Phase 0 stage
+ * list), bit-identical to what sage_quant_prep writes for them.  q is not an
+ * argument: quant->q_codes and quant->q_scale are neither read nor written and
+ * may be NULL; shape->Nq is not used (any value >= 1).  The resulting K/V set
+ * serves sage_attn_fwd_q for queries of any length.  k, v: bf16 device tensors
+ * with strides->k/v (strides->q unused).  Writes k_mean, k_codes, k_scale,
+ * v_codes, v_scale and the workspace.  Errors as for sage_quant_prep.
+ * Launches 3 kernels on `stream`.
+ */
+int sage_quant_prep_kv(const void *k, const void *v, const sage_shape_t *shape, const sage_strides_t *strides,
+                       const sage_quant_t *quant, void *stream);
+
+/*
+ * sage_attn_fwd on bf16 Q: every workgroup first quantizes its own 128-row Q
+ * block by stage 2's rule (A = max|x| over the block's real rows and all
+ * channels, scale = fp32(A/127), code = RNE(fp32(x * fp32(127/A))), the same
+ * arithmetic as sage_quant_prep), then runs stages 3-5 as sage_attn_fwd.  The
+ * codes and scales equal the prep's bit for bit, so the output equals
+ * sage_quant_prep + sage_attn_fwd bit for bit, while the Q codes never pass
+ * through memory.  q: bf16 [B,H,Nq,D] with strides->q (16-byte aligned, strides
+ * multiples of 8 elements); shape->Nq is q's length and may differ from the
+ * one the K/V set was prepared with.  quant: a K/V set from sage_quant_prep_kv
+ * or sage_quant_prep (q_codes, q_scale and the workspace unused, may be NULL).
+ * out as for sage_attn_fwd, and it must not overlap q (SAGE_E_ALIAS).  One
+ * kernel launch on `stream`.
+ */
+int sage_attn_fwd_q(const void *q, const sage_quant_t *quant, const sage_shape_t *shape, float sm_scale,
+                    void *out, const sage_strides_t *strides, void *stream);
+
+/*
  * sage_attn_fwd with the paired schedule (the analogue of the pages' temporal
  * pairing, "Experiment Log", Closed Prior Work, and "Experiment Registry",
  * Complete Registry): each workgroup takes three consecutive 128-row Q blocks

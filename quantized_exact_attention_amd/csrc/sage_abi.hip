@@ -101,13 +101,15 @@ size_t buffer_bytes(const sage_shape_t *s, int which) {
 }
 
 // need_ws: the workspace pointer is required (every entry but the
-// allocation-free prep, which ignores it)
-int check_quant(const sage_quant_t *q, bool need_ws = true) {
-  if (!q || !q->q_codes || !q->q_scale || !q->k_codes || !q->k_scale || !q->v_codes || !q->v_scale ||
-      !q->k_mean || (need_ws && !q->workspace))
+// allocation-free prep, which ignores it); need_q: the Q codes and scale are
+// required (every entry but the K/V-only prep and the Q-quantizing forward,
+// which neither read nor write them)
+int check_quant(const sage_quant_t *q, bool need_ws = true, bool need_q = true) {
+  if (!q || (need_q && (!q->q_codes || !q->q_scale)) || !q->k_codes || !q->k_scale || !q->v_codes ||
+      !q->v_scale || !q->k_mean || (need_ws && !q->workspace))
     return SAGE_E_NULL;
-  if (!aligned16(q->q_codes) || !aligned16(q->k_codes) || !aligned16(q->v_codes) ||
-      (need_ws && !aligned16(q->workspace)) || ((uintptr_t)q->q_scale & 3) || ((uintptr_t)q->k_scale & 3) ||
+  if ((need_q && (!aligned16(q->q_codes) || ((uintptr_t)q->q_scale & 3))) || !aligned16(q->k_codes) ||
+      !aligned16(q->v_codes) || (need_ws && !aligned16(q->workspace)) || ((uintptr_t)q->k_scale & 3) ||
       ((uintptr_t)q->v_scale & 3) || ((uintptr_t)q->k_mean & 3))
     return SAGE_E_ALIGN;
   return SAGE_OK;
@@ -160,11 +162,11 @@ float resolve_sl2(float sm_scale, int D) {
 }
 
 int fill_fwd(const sage_quant_t *q, const sage_shape_t *s, float sm_scale, void *out, const sage_strides_t *st,
-             FwdParams *fp) {
+             FwdParams *fp, bool need_q = true) {
   int r = check_shape(s);
   if (r) return r;
   if (!out || !st) return SAGE_E_NULL;
-  if ((r = check_quant(q, false))) return r;      // the forward does not use the workspace
+  if ((r = check_quant(q, false, need_q))) return r;      // the forward does not use the workspace
   if (!aligned16(out) || check_strides(st->o)) return SAGE_E_ALIGN;
   if (!std::isfinite(sm_scale)) return SAGE_E_ARG;
   if (!rows_disjoint(s, st->o, s->Nq) || overlaps_quant(out, span_bytes(s, st->o, s->Nq), q, s))
@@ -316,23 +318,28 @@ namespace {
 
 // no_alloc: the workspace is the static device scratch instead of quant->workspace;
 // race_seed: nonzero runs the race-gate build of the three launches
+// kv_only: K and V only (q, the Q codes and the Q scale are not used)
 int quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *s, const sage_strides_t *st,
                const sage_quant_t *quant, void *stream, bool single_pass, bool no_alloc = false,
-               uint32_t race_seed = 0) {
+               uint32_t race_seed = 0, bool kv_only = false) {
   int r = check_shape(s);
   if (r) return r;
-  if (!q || !k || !v || !st) return SAGE_E_NULL;
-  if ((r = check_quant(quant, !no_alloc))) return r;
+  if ((!kv_only && !q) || !k || !v || !st) return SAGE_E_NULL;
+  if ((r = check_quant(quant, !no_alloc, !kv_only))) return r;
   sage_quant_t qs = *quant;
+  if (kv_only) {
+    qs.q_codes = nullptr;                        // neither read nor written
+    qs.q_scale = nullptr;
+  }
   if (no_alloc) {
     qs.workspace = nullptr;                      // ignored; the scratch is checked below
     if (buffer_bytes(s, SAGE_BUF_WORKSPACE) > kScratchBytes) return SAGE_E_SCRATCH;
   }
   quant = &qs;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || check_strides(st->q) || check_strides(st->k) ||
-      check_strides(st->v))
+  if ((!kv_only && (!aligned16(q) || check_strides(st->q))) || !aligned16(k) || !aligned16(v) ||
+      check_strides(st->k) || check_strides(st->v))
     return SAGE_E_ALIGN;
-  if (overlaps_quant(q, span_bytes(s, st->q, s->Nq), quant, s) ||
+  if ((!kv_only && overlaps_quant(q, span_bytes(s, st->q, s->Nq), quant, s)) ||
       overlaps_quant(k, span_bytes(s, st->k, s->Nkv), quant, s) ||
       overlaps_quant(v, span_bytes(s, st->v, s->Nkv), quant, s))
     return SAGE_E_ALIAS;
@@ -375,6 +382,7 @@ int quant_prep(const void *q, const void *k, const void *v, const sage_shape_t *
   const int groups = ceil_div(s->Nkv, kFusedRows(s->D));
   // G = 0: statistics, finalize and quantization launches
   p.G = single_pass && groups <= kFusedMaxGroups ? groups : 0;
+  p.kv_only = kv_only;
   p.race_seed = race_seed;
   return launch_prep(p, (hipStream_t)stream) == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
 }
@@ -398,13 +406,40 @@ int sage_quant_prep_no_alloc(const void *q, const void *k, const void *v, const 
   return quant_prep(q, k, v, s, st, quant, stream, false, true);
 }
 
+int sage_quant_prep_kv(const void *k, const void *v, const sage_shape_t *s, const sage_strides_t *st,
+                       const sage_quant_t *quant, void *stream) {
+  return quant_prep(nullptr, k, v, s, st, quant, stream, false, false, 0, true);
+}
+
+int sage_attn_fwd_q(const void *q, const sage_quant_t *quant, const sage_shape_t *s, float sm_scale, void *out,
+                    const sage_strides_t *st, void *stream) {
+  if (!quant) return SAGE_E_NULL;
+  sage_quant_t kv = *quant;
+  kv.q_codes = nullptr;                          // neither read nor written
+  kv.q_scale = nullptr;
+  FwdParams fp;
+  int r = fill_fwd(&kv, s, sm_scale, out, st, &fp, false);
+  if (r) return r;
+  if (!q) return SAGE_E_NULL;
+  if (!aligned16(q) || check_strides(st->q)) return SAGE_E_ALIGN;
+  if (overlap(out, span_bytes(s, st->o, s->Nq), q, span_bytes(s, st->q, s->Nq))) return SAGE_E_ALIAS;
+  if ((r = device_ok())) return r;
+  fp.q = (const uint16_t *)q;
+  for (int i = 0; i < 3; ++i) fp.qs[i] = st->q[i];
+  fp.q_codes = nullptr;
+  fp.q_scale = nullptr;
+  return launch_fwd(fp, s->D, fp.n_units, FwdVariant::kQuantizeQ, (hipStream_t)stream) == hipSuccess
+             ? SAGE_OK
+             : SAGE_E_LAUNCH;
+}
+
 int sage_attn_fwd(const sage_quant_t *quant, const sage_shape_t *s, float sm_scale, void *out,
                   const sage_strides_t *st, void *stream) {
   FwdParams fp;
   int r = fill_fwd(quant, s, sm_scale, out, st, &fp);
   if (r) return r;
   if ((r = device_ok())) return r;
-  return launch_fwd(fp, s->D, fp.n_units, false, false, false, (hipStream_t)stream) == hipSuccess ? SAGE_OK
+  return launch_fwd(fp, s->D, fp.n_units, FwdVariant::kDefault, (hipStream_t)stream) == hipSuccess ? SAGE_OK
                                                                                                    : SAGE_E_LAUNCH;
 }
 
@@ -414,7 +449,7 @@ int sage_attn_fwd_paired(const sage_quant_t *quant, const sage_shape_t *s, float
   int r = fill_fwd(quant, s, sm_scale, out, st, &fp);
   if (r) return r;
   if ((r = device_ok())) return r;
-  return launch_fwd(fp, s->D, fp.n_units, false, false, true, (hipStream_t)stream) == hipSuccess ? SAGE_OK
+  return launch_fwd(fp, s->D, fp.n_units, FwdVariant::kPaired, (hipStream_t)stream) == hipSuccess ? SAGE_OK
                                                                                                   : SAGE_E_LAUNCH;
 }
 
@@ -438,7 +473,7 @@ int sage_attn_fwd_capture(const sage_quant_t *quant, const sage_shape_t *s, floa
   fp.part_cap = part_cap;
   fp.ro_cap = ro_cap;
   fp.r_cap = r_cap;
-  return launch_fwd(fp, s->D, n_units, true, false, false, (hipStream_t)stream) == hipSuccess ? SAGE_OK
+  return launch_fwd(fp, s->D, n_units, FwdVariant::kCapture, (hipStream_t)stream) == hipSuccess ? SAGE_OK
                                                                                                : SAGE_E_LAUNCH;
 }
 
@@ -454,7 +489,7 @@ int sage_race_gate(const void *q, const void *k, const void *v, const sage_shape
     return SAGE_E_ALIAS;
   if ((r = quant_prep(q, k, v, s, st, quant, stream, false, false, seed))) return r;
   fp.race_seed = seed;
-  return launch_fwd(fp, s->D, fp.n_units, false, true, false, (hipStream_t)stream) == hipSuccess ? SAGE_OK
+  return launch_fwd(fp, s->D, fp.n_units, FwdVariant::kRace, (hipStream_t)stream) == hipSuccess ? SAGE_OK
                                                                                                  : SAGE_E_LAUNCH;
 }
 

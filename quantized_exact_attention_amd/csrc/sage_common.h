@@ -37,6 +37,7 @@ struct PrepParams {
   double *ws_asum;                // single-pass path: [B*H][D] K column sums (atomic, exact)
   uint32_t *ws_amax;              // single-pass path: [B*H][D] V column max |v| (float bits, atomic max)
   int G;                          // single-pass path: K/V workgroups per (b,h); 0 selects three launches
+  int kv_only;                    // three launches without the Q blocks (q, q_codes, q_scale unused)
   uint32_t race_seed;             // nonzero: the race-gate build of the three launches (tests only)
 };
 
@@ -61,7 +62,36 @@ struct FwdParams {
   float *ro_cap;                  // [unit][128][T][D]: RO after tile j
   float *r_cap;                   // [unit][128]: reciprocal of 448*d
   uint32_t race_seed;             // race-gate build only
+  // Q-quantizing build only: bf16 Q and its element strides (b, h, n); q_codes
+  // and q_scale are not read
+  const uint16_t *q;
+  int64_t qs[3];
 };
+
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Eight bf16 values (16 bytes, element order) as float32 (exact).
+__device__ __forceinline__ void unpack8(const uint4 &x, float *f) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// Four INT8 codes, byte e = clamp(RNE(fp32(x[e] * inv)), -127, 127): the
+// quantization rule of Q and K blocks (inv = fp32(127 / absmax)).
+__device__ __forceinline__ uint32_t pack_i8x4(const float *x, float inv) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float q = __builtin_rintf(x[e] * inv);          // fp32 product, round half to even
+    q = fminf(fmaxf(q, -127.f), 127.f);
+    w |= ((uint32_t)(int32_t)q & 0xffu) << (8 * e);
+  }
+  return w;
+}
 
 // Race gate (test builds only).  A wave-uniform pseudo-random pause of 0, 64,
 // 256 or 1024 cycles, drawn from (seed, workgroup, wave, site, step), placed
@@ -105,9 +135,10 @@ hipError_t launch_prep(const PrepParams &p, hipStream_t stream);
 // Q blocks per workgroup of the paired forward schedule
 constexpr int kPairedBlocks = 3;
 
-// race: the race-gate build (p.race_seed nonzero); paired: the paired schedule;
-// at most one of capture, race and paired
-hipError_t launch_fwd(const FwdParams &p, int D, int grid, bool capture, bool race, bool paired,
-                      hipStream_t stream);
+// Forward builds: the default schedule, the capture build (checkpoints of the
+// listed units), the race-gate build (p.race_seed nonzero), the paired schedule,
+// and the build that quantizes each Q block itself from bf16 Q (p.q).
+enum class FwdVariant { kDefault, kCapture, kRace, kPaired, kQuantizeQ };
+hipError_t launch_fwd(const FwdParams &p, int D, int grid, FwdVariant variant, hipStream_t stream);
 
 }  // namespace sage

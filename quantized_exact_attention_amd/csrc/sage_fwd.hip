@@ -9,7 +9,9 @@
 // named in Phase 2B Fixed Aligned Numerical Prototype (QK, m, d, FP8
 // probability, rescale, PV partial, RO, reciprocal, BF16 output); the race-gate
 // build (RACE) adds seeded pauses before every LDS access and tile copy; QPW
-// selects one Q block per workgroup (default) or the paired schedule.
+// selects one Q block per workgroup (default) or the paired schedule; the
+// Q-quantizing build (QIN) takes bf16 Q and quantizes its block in the
+// prologue instead of reading the prep's codes.
 //
 // Work decomposition: one workgroup = 4 wavefronts = one 128-row Q block of one
 // (b,h); each wavefront owns 32 query rows and walks all 64-key tiles in order.
@@ -313,13 +315,66 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   __syncthreads();
 }
 
+// Q-quantizing build: the workgroup's 128-row Q block from bf16 Q, by the rule
+// of the prep stage (absmax over the block's real rows and all channels, scale
+// = absmax / 127, code = clamp(RNE(fp32(x * fp32(127 / absmax))))), so the
+// codes and the scale equal the prep's bit for bit.  Lane l of wave wq holds
+// row wq*32 + l%32 and, per k-step s, channels 32 s + 16 (l/32) .. +15: exactly
+// the 16 bytes of the B operand it reads from the prep's code buffer.  The
+// four wave maxima meet in `red` (16 bytes of LDS not yet used by the tile
+// ring).  Returns the block's scale.
+template <int D>
+__device__ __forceinline__ float quantize_q_operand(const FwdParams &p, int bh, int qb, int wq, int lane, float *red,
+                                                    v4i *qop) {
+  constexpr int NS = D / 32;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int n = qb * kBQ + wq * 32 + (lane & 31);
+  uint4 raw[2 * NS];
+  if (n < p.Nq) {                               // rows past Nq are zero and do not raise the max
+    const uint16_t *row = p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)n * p.qs[2] + 16 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      raw[2 * s] = *(const uint4 *)(row + 32 * s);
+      raw[2 * s + 1] = *(const uint4 *)(row + 32 * s + 8);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2 * NS; ++i) raw[i] = make_uint4(0, 0, 0, 0);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2 * NS; ++i) {
+    float f[8];
+    unpack8(raw[i], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if (lane == 0) red[wq] = amax;
+  __syncthreads();
+  const float A = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = A > 0.f ? 127.0f / A : 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    float lo[8], hi[8];
+    unpack8(raw[2 * s], lo);
+    unpack8(raw[2 * s + 1], hi);
+    qop[s] = v4i{(int)pack_i8x4(lo, inv), (int)pack_i8x4(lo + 4, inv), (int)pack_i8x4(hi, inv),
+                 (int)pack_i8x4(hi + 4, inv)};
+  }
+  return A > 0.f ? A / 127.0f : 0.f;
+}
+
 // QPW: 128-row Q blocks per workgroup.  1 is the default schedule; 3 is the
 // paired schedule (the analogue of temporal pairing, "Experiment Log", Closed
 // Prior Work, and the split variants of the Phase 1 decision): three Q blocks
 // of one (b,h), twelve waves, share one K/V tile stream through LDS, so each
 // K/V tile is copied from L2 once per three blocks instead of once per block.
-template <int D, bool CAP, bool RACE, int QPW>
+// QIN: the Q-quantizing build (default schedule only).
+template <int D, bool CAP, bool RACE, int QPW, bool QIN = false>
 __global__ __launch_bounds__(256 * QPW, FwdOccupancy<D>::waves_per_simd) void k_attn_fwd(FwdParams p) {
+  static_assert(!QIN || (QPW == 1 && !CAP && !RACE), "Q quantization in the default schedule only");
   constexpr int NS = D / 32;                 // INT8 k-steps per key row == PV row blocks
   constexpr int TILE = kBK * D;              // bytes of one K (or V) tile
   // two LDS buffers of [K tile | V tile], alternating per tile
@@ -354,12 +409,17 @@ __global__ __launch_bounds__(256 * QPW, FwdOccupancy<D>::waves_per_simd) void k_
 
   // Q^T operand (B of the INT8 product) for this wave's 32 rows, kept in registers.
   v4i qop[NS];
-  {
+  float sq;
+  if (QIN) {
+    // lds_b is first written by tile 0's step, after the barrier below
+    sq = quantize_q_operand<D>(p, bh, qb, wq, lane, (float *)lds_b, qop);
+    sq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sq)));   // uniform: keep it scalar
+  } else {
     const int8_t *qsrc = p.q_codes + ((size_t)u * 4 + wq) * (NS * 1024) + lane * 16;
 #pragma unroll
     for (int s = 0; s < NS; ++s) qop[s] = *(const v4i *)(qsrc + s * 1024);
+    sq = load_uniform(p.q_scale + u);
   }
-  const float sq = load_uniform(p.q_scale + u);
   const int row = wq * 32 + (lane & 31);
 
   FwdState<D> st;
@@ -412,23 +472,32 @@ __global__ __launch_bounds__(256 * QPW, FwdOccupancy<D>::waves_per_simd) void k_
 }
 
 template <int D>
-static void launch_fwd_d(const FwdParams &p, int grid, bool capture, bool race, bool paired, hipStream_t st) {
-  if (capture) {
-    hipLaunchKernelGGL((k_attn_fwd<D, true, false, 1>), dim3(grid), dim3(256), 0, st, p);
-  } else if (race) {
-    hipLaunchKernelGGL((k_attn_fwd<D, false, true, 1>), dim3(grid), dim3(256), 0, st, p);
-  } else if (paired) {
-    const int groups = (p.n_units / p.nqb) * ((p.nqb + kPairedBlocks - 1) / kPairedBlocks);
-    hipLaunchKernelGGL((k_attn_fwd<D, false, false, kPairedBlocks>), dim3(groups), dim3(256 * kPairedBlocks), 0,
-                       st, p);
-  } else {
-    hipLaunchKernelGGL((k_attn_fwd<D, false, false, 1>), dim3(grid), dim3(256), 0, st, p);
+static void launch_fwd_d(const FwdParams &p, int grid, FwdVariant variant, hipStream_t st) {
+  switch (variant) {
+    case FwdVariant::kCapture:
+      hipLaunchKernelGGL((k_attn_fwd<D, true, false, 1>), dim3(grid), dim3(256), 0, st, p);
+      break;
+    case FwdVariant::kRace:
+      hipLaunchKernelGGL((k_attn_fwd<D, false, true, 1>), dim3(grid), dim3(256), 0, st, p);
+      break;
+    case FwdVariant::kPaired: {
+      const int groups = (p.n_units / p.nqb) * ((p.nqb + kPairedBlocks - 1) / kPairedBlocks);
+      hipLaunchKernelGGL((k_attn_fwd<D, false, false, kPairedBlocks>), dim3(groups), dim3(256 * kPairedBlocks), 0,
+                         st, p);
+      break;
+    }
+    case FwdVariant::kQuantizeQ:
+      hipLaunchKernelGGL((k_attn_fwd<D, false, false, 1, true>), dim3(grid), dim3(256), 0, st, p);
+      break;
+    default:
+      hipLaunchKernelGGL((k_attn_fwd<D, false, false, 1>), dim3(grid), dim3(256), 0, st, p);
+      break;
   }
 }
 
-hipError_t launch_fwd(const FwdParams &p, int D, int grid, bool capture, bool race, bool paired, hipStream_t st) {
-  if (D == 128) launch_fwd_d<128>(p, grid, capture, race, paired, st);
-  else launch_fwd_d<64>(p, grid, capture, race, paired, st);
+hipError_t launch_fwd(const FwdParams &p, int D, int grid, FwdVariant variant, hipStream_t st) {
+  if (D == 128) launch_fwd_d<128>(p, grid, variant, st);
+  else launch_fwd_d<64>(p, grid, variant, st);
   return hipGetLastError();
 }
 

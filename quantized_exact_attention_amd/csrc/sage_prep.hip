@@ -13,17 +13,6 @@
 
 namespace sage {
 
-__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-__device__ __forceinline__ void unpack8(const uint4 &x, float *f) {
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-
 // Max of a non-negative float over the 256-thread block (bit order == value order).
 // RACE: the race-gate build (pauses before the LDS write and read).
 template <bool RACE = false>
@@ -50,17 +39,6 @@ template <int D>
 __device__ __forceinline__ int i8_operand_offset(int r, int c16) {
   const int g = r >> 5, lane = (r & 31) + 32 * (c16 & 1), s = c16 >> 1;
   return ((g * (D / 32) + s) * 64 + lane) * 16;
-}
-
-__device__ __forceinline__ uint32_t pack_i8x4(const float *x, float inv) {
-  uint32_t w = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float q = __builtin_rintf(x[e] * inv);          // fp32 product, round half to even
-    q = fminf(fmaxf(q, -127.f), 127.f);
-    w |= ((uint32_t)(int32_t)q & 0xffu) << (8 * e);
-  }
-  return w;
 }
 
 // ---- 1. per (b,h, key chunk): FP64 column sums of K (exact for bf16 data) and
@@ -571,7 +549,8 @@ static hipError_t launch_prep_d(const PrepParams &p, hipStream_t st) {
     hipLaunchKernelGGL((k_prep_pass2<D, true>), dim3(p.T, BH), dim3(256), 0, st, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((k_prep_pass1<D, false>), dim3(p.nchunk + p.nqb, BH), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((k_prep_pass1<D, false>), dim3(p.nchunk + (p.kv_only ? 0 : p.nqb), BH), dim3(256), 0, st,
+                     p);
   hipLaunchKernelGGL((k_prep_finalize<D, false>), dim3(BH, D / 16), dim3(256), 0, st, p);
   hipLaunchKernelGGL((k_prep_pass2<D, false>), dim3(p.T, BH), dim3(256), 0, st, p);
   return hipGetLastError();

@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(SageStrides), vp]
         L.sage_attn_fwd_capture.argtypes = [ctypes.POINTER(SageQuantC), ctypes.POINTER(SageShape), f32, vp,
                                             ctypes.POINTER(SageStrides), vp, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.sage_quant_prep_kv.argtypes = [vp, vp, ctypes.POINTER(SageShape), ctypes.POINTER(SageStrides),
+                                         ctypes.POINTER(SageQuantC), vp]
+        L.sage_attn_fwd_q.argtypes = [vp, ctypes.POINTER(SageQuantC), ctypes.POINTER(SageShape), f32, vp,
+                                      ctypes.POINTER(SageStrides), vp]
         L.sage_clock_sample.argtypes = [vp, vp]
         L.sage_mfma_peak_sample.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
         L.sage_device_check.argtypes = [ctypes.c_int]
@@ -78,7 +82,8 @@ def lib() -> ctypes.CDLL:
         L.sage_status_string.restype = ctypes.c_char_p
         for name in ("sage_buffer_bytes", "sage_prep_status_offset", "sage_quant_prep",
                      "sage_quant_prep_single_pass", "sage_attn_fwd", "sage_attn_fwd_paired", "sage_attn_fwd_capture",
-                     "sage_device_check", "sage_clock_sample", "sage_mfma_peak_sample"):
+                     "sage_device_check", "sage_clock_sample", "sage_mfma_peak_sample", "sage_quant_prep_kv",
+                     "sage_attn_fwd_q"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -116,14 +121,17 @@ def _strides3(t: torch.Tensor):
 
 @dataclass
 class SageQuant:
-    """Device buffers of the quantized operands (see sage_quant_t in the header)."""
+    """Device buffers of the quantized operands (see sage_quant_t in the header).
+
+    A K/V-only set (from sage_quant_prep_kv) has q_codes = q_scale = None and
+    serves sage_attn_fwd_q for queries of any length."""
     B: int
     H: int
     Nq: int
     Nkv: int
     D: int
-    q_codes: torch.Tensor
-    q_scale: torch.Tensor
+    q_codes: torch.Tensor | None
+    q_scale: torch.Tensor | None
     k_codes: torch.Tensor
     k_scale: torch.Tensor
     v_codes: torch.Tensor
@@ -146,22 +154,33 @@ class SageQuant:
     def T(self) -> int:
         return -(-self.Nkv // BK)
 
-    def _key(self, device):
-        bufs = [getattr(self, n) for n in BUFFERS]
-        if not all(isinstance(t, torch.Tensor) for t in bufs):
-            return None
-        return (device,) + tuple((t.data_ptr(), t.numel(), t.is_contiguous(), t.device) for t in bufs)
+    @property
+    def kv_only(self) -> bool:
+        return self.q_codes is None and self.q_scale is None
 
-    def check_buffers(self, device: torch.device):
+    @property
+    def device(self) -> torch.device:
+        return self.k_codes.device
+
+    def _key(self, device, need_q):
+        bufs = [getattr(self, n) for n in BUFFERS]
+        if not all(isinstance(t, torch.Tensor) or t is None for t in bufs):
+            return None
+        return (device, need_q) + tuple(None if t is None else (t.data_ptr(), t.numel(), t.is_contiguous(),
+                                                                 t.device) for t in bufs)
+
+    def check_buffers(self, device: torch.device, need_q: bool = True):
         """Every buffer on `device`, contiguous and at least as large as the C
-        ABI's size for this shape (a caller-built or reused set included).
-        The outcome is remembered for the same buffers, so repeated calls on
-        one set cost one address comparison."""
-        key = self._key(device)
+        ABI's size for this shape (a caller-built or reused set included); the
+        Q codes and scale only if need_q.  The outcome is remembered for the
+        same buffers, so repeated calls on one set cost one address comparison."""
+        key = self._key(device, need_q)
         if key is not None and key == self._checked:
             return
         for i, name in enumerate(BUFFERS):
             t = getattr(self, name)
+            if not need_q and name in ("q_codes", "q_scale"):
+                continue
             if not isinstance(t, torch.Tensor) or t.device != device or not t.is_contiguous():
                 raise ValueError("quant.%s must be a contiguous tensor on %s" % (name, device))
             if t.numel() * t.element_size() < sage_buffer_bytes(self.B, self.H, self.Nq, self.Nkv, self.D, i):
@@ -178,16 +197,19 @@ class SageQuant:
         return int(self.workspace[off.value:off.value + 4].cpu().view(torch.int32).item())
 
     def c_struct(self) -> SageQuantC:
-        ptrs = tuple(getattr(self, n).data_ptr() for n in BUFFERS)
+        ptrs = tuple(0 if getattr(self, n) is None else getattr(self, n).data_ptr() for n in BUFFERS)
         if self._cstruct is None or self._cstruct[0] != ptrs:
             self._cstruct = (ptrs, SageQuantC(*ptrs))
         return self._cstruct[1]
 
     @classmethod
-    def allocate(cls, B, H, Nq, Nkv, D, device) -> "SageQuant":
+    def allocate(cls, B, H, Nq, Nkv, D, device, kv_only: bool = False) -> "SageQuant":
         dt = {"q_codes": torch.int8, "k_codes": torch.int8, "v_codes": torch.uint8, "workspace": torch.uint8}
         bufs = {}
         for i, name in enumerate(BUFFERS):
+            if kv_only and name in ("q_codes", "q_scale"):
+                bufs[name] = None
+                continue
             nbytes = sage_buffer_bytes(B, H, Nq, Nkv, D, i)
             dtype = dt.get(name, torch.float32)
             count = nbytes // torch.empty(0, dtype=dtype).element_size()
@@ -228,12 +250,67 @@ def sage_quant_prep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Sage
     return quant
 
 
+def sage_quant_prep_kv(k: torch.Tensor, v: torch.Tensor, out: SageQuant | None = None, stream=None) -> SageQuant:
+    """K mean, K smoothing, INT8 K per tile and FP8 V per channel only: the
+    K/V set that sage_attn_fwd_q uses for queries of any length (Q is
+    quantized inside that forward)."""
+    for t in (k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("k, v must be bfloat16 CUDA tensors")
+    if k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("k and v must be [B,H,Nkv,D] of one shape")
+    if v.device != k.device:
+        raise ValueError("k and v must be on one device")
+    B, H, Nkv, D = k.shape
+    if out is None:
+        quant = SageQuant.allocate(B, H, 1, Nkv, D, k.device, kv_only=True)
+    else:
+        if (out.B, out.H, out.Nkv, out.D) != (B, H, Nkv, D):
+            raise ValueError("out was allocated for another shape")
+        out.check_buffers(k.device, need_q=False)
+        quant = out
+    st = SageStrides()
+    st.k, st.v = _strides3(k), _strides3(v)
+    qc = quant.c_struct()
+    _check(lib().sage_quant_prep_kv(k.data_ptr(), v.data_ptr(), ctypes.byref(quant.shape), ctypes.byref(st),
+                                    ctypes.byref(qc), _stream_handle(stream, k.device)), "sage_quant_prep_kv")
+    return quant
+
+
+def sage_attn_fwd_q(q: torch.Tensor, quant: SageQuant, sm_scale: float | None = None,
+                    out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The forward on bf16 Q: each workgroup quantizes its Q block by the prep's
+    rule, then runs the default forward on the K/V set `quant` (from
+    sage_quant_prep_kv or sage_quant_prep).  Same output as sage_quant_prep +
+    sage_attn_fwd, bit for bit.  Returns bf16 [B,H,Nq,D]."""
+    if q.dtype != torch.bfloat16 or not q.is_cuda or q.dim() != 4:
+        raise TypeError("q must be a bfloat16 CUDA tensor [B,H,Nq,D]")
+    B, H, Nq, D = q.shape
+    if (B, H, D) != (quant.B, quant.H, quant.D):
+        raise ValueError("q does not match the K/V set's B, H, D")
+    if q.device != quant.device:
+        raise ValueError("q must be on the device of the quantized buffers")
+    quant.check_buffers(q.device, need_q=False)
+    if out is None:
+        out = torch.empty(B, H, Nq, D, dtype=torch.bfloat16, device=q.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, Nq, D) or out.device != q.device:
+        raise ValueError("out must be bfloat16 [B,H,Nq,D] on the device of q")
+    shape = SageShape(B, H, Nq, quant.Nkv, D)
+    st = SageStrides()
+    st.q, st.o = _strides3(q), _strides3(out)
+    qc = quant.c_struct()
+    _check(lib().sage_attn_fwd_q(q.data_ptr(), ctypes.byref(qc), ctypes.byref(shape),
+                                 ctypes.c_float(0.0 if sm_scale is None else sm_scale), out.data_ptr(),
+                                 ctypes.byref(st), _stream_handle(stream, q.device)), "sage_attn_fwd_q")
+    return out
+
+
 def _out_tensor(quant: SageQuant, out):
     if out is None:
-        out = torch.empty(quant.B, quant.H, quant.Nq, quant.D, dtype=torch.bfloat16, device=quant.q_codes.device)
+        out = torch.empty(quant.B, quant.H, quant.Nq, quant.D, dtype=torch.bfloat16, device=quant.device)
     if out.dtype != torch.bfloat16 or tuple(out.shape) != (quant.B, quant.H, quant.Nq, quant.D):
         raise ValueError("out must be bfloat16 [B,H,Nq,D]")
-    if out.device != quant.q_codes.device:
+    if out.device != quant.device:
         raise ValueError("out must be on the device of the quantized buffers")
     quant.check_buffers(out.device)
     return out
@@ -265,7 +342,7 @@ def sage_attn_fwd_capture(quant: SageQuant, units, sm_scale: float | None = None
     float32 [n,128,T,D], r float32 [n,128] (1/(448*d)).
     """
     out = _out_tensor(quant, out)
-    dev = quant.q_codes.device
+    dev = quant.device
     units_t = torch.as_tensor(list(units), dtype=torch.int32).to(dev)
     n = units_t.numel()
     T = quant.T

@@ -218,3 +218,46 @@ def test_mfma_peak_sample_validation_before_any_hip_call(L, no_gfx950):
     for kind, iters in ((2, 16), (-1, 16), (0, 0), (1, -5), (1, 65537)):
         assert f(kind, iters, dst, None) == -8, (kind, iters)
     assert f(1, 65536, dst, None) in (0, -6, -7)
+
+
+def test_kv_prep_validation_before_any_hip_call(L, no_gfx950):
+    """The K/V-only prep takes no q and accepts NULL Q codes and scale."""
+    f = L.sage_quant_prep_kv
+    shape = sage.SageShape(1, 2, 1, 100, 64)
+    st = _strides(1, 2, 100, 64)
+    qc = _fake_quant()
+    qc.q_codes = None
+    qc.q_scale = None
+    k, v = 2 << 36, 3 << 36
+    assert f(None, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(qc), None) == -1
+    assert f(k, v, ctypes.byref(shape), None, ctypes.byref(qc), None) == -1
+    assert f(k + 4, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(qc), None) == -4
+    nokm = _fake_quant()
+    nokm.q_codes = None
+    nokm.k_mean = None
+    assert f(k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(nokm), None) == -1
+    alias = _fake_quant(base=k)                  # q_codes (ignored) at k; k_codes right after it
+    alias.q_codes = None
+    alias.k_codes = k
+    assert f(k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(alias), None) == -5
+    assert f(k, v, ctypes.byref(shape), ctypes.byref(st), ctypes.byref(qc), None) in (0, -6, -7)
+
+
+def test_q_quantizing_fwd_validation_before_any_hip_call(L, no_gfx950):
+    f = L.sage_attn_fwd_q
+    shape = sage.SageShape(2, 2, 300, 128, 128)
+    st = _strides(2, 2, 300, 128)
+    qc = _fake_quant()
+    qc.q_codes = None
+    qc.q_scale = None
+    qc.workspace = None
+    q, out = 1 << 45, (1 << 45) + (1 << 36)
+    assert f(None, ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(st), None) == -1
+    assert f(q, ctypes.byref(qc), ctypes.byref(shape), 0.0, None, ctypes.byref(st), None) == -1
+    assert f(q + 8, ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(st), None) == -4
+    bad = _strides(2, 2, 300, 128)
+    bad.q[2] = 132
+    assert f(q, ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(bad), None) == -4
+    assert f(q, ctypes.byref(qc), ctypes.byref(shape), 0.0, q + 256, ctypes.byref(st), None) == -5
+    assert f(q, ctypes.byref(qc), ctypes.byref(shape), float("nan"), out, ctypes.byref(st), None) == -8
+    assert f(q, ctypes.byref(qc), ctypes.byref(shape), 0.0, out, ctypes.byref(st), None) in (0, -6, -7)

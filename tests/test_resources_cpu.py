@@ -45,8 +45,8 @@ def report():
     return rep
 
 
-def _fwd(report, D, capture, race, qpw):
-    name = "_ZN4sage10k_attn_fwdILi%dELb%dELb%dELi%dEEEvNS_9FwdParamsE" % (D, capture, race, qpw)
+def _fwd(report, D, capture, race, qpw, qin=0):
+    name = "_ZN4sage10k_attn_fwdILi%dELb%dELb%dELi%dELb%dEEEvNS_9FwdParamsE" % (D, capture, race, qpw, qin)
     assert name in report, sorted(report)
     return report[name]
 
@@ -54,7 +54,7 @@ def _fwd(report, D, capture, race, qpw):
 def test_every_kernel_but_the_capture_build_runs_without_scratch(report):
     assert len(report) >= 20
     for name, r in report.items():
-        if "k_attn_fwd" in name and "Lb1ELb0ELi1E" in name:      # capture build: tests only
+        if "k_attn_fwd" in name and "Lb1ELb0ELi1ELb0E" in name:      # capture build: tests only
             continue
         assert r["ScratchSize"] == 0, (name, r)
 
@@ -66,7 +66,8 @@ def test_default_forward_keeps_its_occupancy(report, D, waves):
     assert r["LDS"] == 2 * 2 * 64 * D                       # two [K tile | V tile] buffers
 
 
-def test_race_gate_and_paired_builds_match_the_default_occupancy(report):
+def test_race_gate_paired_and_q_quantizing_builds_match_the_default_occupancy(report):
     for D, waves in ((128, 3), (64, 5)):
-        for capture, race, qpw in ((0, 1, 1), (0, 0, 3)):
-            assert _fwd(report, D, capture, race, qpw)["Occupancy"] == waves
+        for capture, race, qpw, qin in ((0, 1, 1, 0), (0, 0, 3, 0), (0, 0, 1, 1)):
+            r = _fwd(report, D, capture, race, qpw, qin)
+            assert r["Occupancy"] == waves and r["ScratchSize"] == 0, r
