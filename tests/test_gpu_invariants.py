@@ -82,21 +82,30 @@ def test_thousand_launches_bit_identical():
     assert int(mismatches) == 0
 
 
-@pytest.mark.parametrize("single_pass", [False, True])
-def test_graph_capture_replay_matches_eager(single_pass):
+@pytest.mark.parametrize("mode", ["three_launches", "single_pass", "q_quantizing_pair"])
+def test_graph_capture_replay_matches_eager(mode):
     w = WORKLOADS["ragged_tails"]
     q, k, v = make_inputs(w, seed=21, B=1, H=4, Nq=500, Nkv=700, D=128)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
-    quant = sage.sage_quant_prep(qd, kd, vd, single_pass=single_pass)
-    out = sage.sage_attn_fwd(quant)
+    single_pass = mode == "single_pass"
+    if mode == "q_quantizing_pair":
+        quant = sage.sage_quant_prep_kv(kd, vd)
+        out = sage.sage_attn_fwd_q(qd, quant)
+    else:
+        quant = sage.sage_quant_prep(qd, kd, vd, single_pass=single_pass)
+        out = sage.sage_attn_fwd(quant)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            sage.sage_quant_prep(qd, kd, vd, out=quant, single_pass=single_pass)
-            sage.sage_attn_fwd(quant, out=out)
+            if mode == "q_quantizing_pair":
+                sage.sage_quant_prep_kv(kd, vd, out=quant)
+                sage.sage_attn_fwd_q(qd, quant, out=out)
+            else:
+                sage.sage_quant_prep(qd, kd, vd, out=quant, single_pass=single_pass)
+                sage.sage_attn_fwd(quant, out=out)
     torch.cuda.current_stream().wait_stream(s)
     for r in range(4):
         # new inputs written in place, then replay, then compare with an eager run
@@ -135,19 +144,25 @@ def test_binding_rejects_mismatched_buffers():
     assert torch.equal(sage.sage_attn_fwd(quant), ref)                  # the set is still usable
 
 
-@pytest.mark.parametrize("single_pass", [False, True])
-def test_calls_with_preallocated_buffers_allocate_nothing(single_pass):
+@pytest.mark.parametrize("mode", ["three_launches", "single_pass", "q_quantizing_pair"])
+def test_calls_with_preallocated_buffers_allocate_nothing(mode):
     """With the quantized set and the output passed in, prep + forward make no
     device allocation (torch's allocator counts every request, cached or not):
     the path a captured graph or an allocation-free caller relies on."""
     q, k, v = (t.to(DEV) for t in make_inputs(WORKLOADS["ragged_tails"], seed=8, B=1, H=3, Nq=200, Nkv=300, D=128))
-    quant = sage.sage_quant_prep(q, k, v, single_pass=single_pass)
-    out = sage.sage_attn_fwd(quant)
+    single_pass = mode == "single_pass"
+    pair = mode == "q_quantizing_pair"
+    quant = sage.sage_quant_prep_kv(k, v) if pair else sage.sage_quant_prep(q, k, v, single_pass=single_pass)
+    out = sage.sage_attn_fwd_q(q, quant) if pair else sage.sage_attn_fwd(quant)
     torch.cuda.synchronize()
     before = torch.cuda.memory_stats(DEV)["allocation.all.allocated"]
     for _ in range(3):
-        sage.sage_quant_prep(q, k, v, out=quant, single_pass=single_pass)
-        sage.sage_attn_fwd(quant, out=out)
+        if pair:
+            sage.sage_quant_prep_kv(k, v, out=quant)
+            sage.sage_attn_fwd_q(q, quant, out=out)
+        else:
+            sage.sage_quant_prep(q, k, v, out=quant, single_pass=single_pass)
+            sage.sage_attn_fwd(quant, out=out)
     torch.cuda.synchronize()
     assert torch.cuda.memory_stats(DEV)["allocation.all.allocated"] == before
     assert torch.equal(_bits(out), _bits(sage.sage_attention(q, k, v)))
