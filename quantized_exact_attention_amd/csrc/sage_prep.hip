@@ -505,7 +505,7 @@ __device__ __forceinline__ void fused_kv_group(const PrepParams &p, int bh, int 
 template <int D>
 __global__ __launch_bounds__(256) void k_prep_fused(PrepParams p) {
   __shared__ FusedSmem<D> sm;
-  const int per = p.G + p.nqb;
+  const int per = p.G + (p.kv_only ? 0 : p.nqb);
   const int bh = blockIdx.x / per, r = blockIdx.x - bh * per;
   if (r < p.G) fused_kv_group<D>(p, bh, r, sm);
   else quant_q_block<D>(p, r - p.G, bh, &sm.red[0][0]);
@@ -540,7 +540,7 @@ static hipError_t launch_prep_d(const PrepParams &p, hipStream_t st) {
   if (p.G > 0) {
     const int nsync = (int)ws_sync_words(BH, D);
     hipLaunchKernelGGL(k_prep_clear, dim3((nsync + 255) / 256), dim3(256), 0, st, p.ws_sync, nsync);
-    hipLaunchKernelGGL(k_prep_fused<D>, dim3(BH * p.G + BH * p.nqb), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_prep_fused<D>, dim3(BH * (p.G + (p.kv_only ? 0 : p.nqb))), dim3(256), 0, st, p);
     return hipGetLastError();
   }
   if (p.race_seed) {

@@ -367,8 +367,10 @@ def sage_attn_fwd_capture(quant: SageQuant, units, sm_scale: float | None = None
 
 
 def sage_attention(q, k, v, sm_scale: float | None = None) -> torch.Tensor:
-    """Both calls of the hot path: prep then fused forward."""
-    return sage_attn_fwd(sage_quant_prep(q, k, v), sm_scale)
+    """The whole hot path on bf16 q, k, v: the K/V prep, then the forward that
+    quantizes its own Q blocks (the same output bits as sage_quant_prep +
+    sage_attn_fwd, without the Q codes' round trip through memory)."""
+    return sage_attn_fwd_q(q, sage_quant_prep_kv(k, v), sm_scale)
 
 
 CLOCK_SAMPLES = 2048
