@@ -119,3 +119,31 @@ def test_full_size_bit_identical(name):
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
     del ref, got, kv
     torch.cuda.empty_cache()
+
+
+def _sweep_cases(n=40):
+    rng = np.random.default_rng(77)
+    cases = []
+    for i in range(n):
+        D = int(rng.choice([64, 128]))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 5))
+        Nq, Nkv = int(rng.integers(1, 1500)), int(rng.integers(1, 1500))
+        dist = str(rng.choice(["dit_block", "ragged_tails", "headdim64"]))   # no / 3% / 1% outliers
+        sm = None if rng.random() < 0.7 else float(rng.uniform(0.02, 0.3))
+        strided = bool(rng.random() < 0.3)
+        cases.append((i, dist, B, H, Nq, Nkv, D, sm, strided))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: "s%d_%s_%dx%dx%dx%dx%d" % (c[0], c[1], *c[2:7]))
+def test_random_shapes_bit_identical_to_the_two_calls(case):
+    i, dist, B, H, Nq, Nkv, D, sm, strided = case
+    q, k, v = make_inputs(WORKLOADS[dist], seed=500 + i, B=B, H=H, Nq=Nq, Nkv=Nkv, D=D)
+    if strided:
+        qd, kd, vd = (t.transpose(1, 2).contiguous().to(DEV).transpose(1, 2) for t in (q, k, v))
+    else:
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ref = sage.sage_attn_fwd(sage.sage_quant_prep(qd, kd, vd), sm)
+    got = sage.sage_attn_fwd_q(qd, sage.sage_quant_prep_kv(kd, vd), sm)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(got), _bits(ref))
