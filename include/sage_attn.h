@@ -84,6 +84,9 @@ typedef struct sage_strides {
  *           contents before a call do not matter (each call initializes what
  *           it reads); two prep calls must not use one workspace at the same
  *           time.
+ * sage_quant_prep_kv and sage_attn_fwd_q neither read nor write q_codes and
+ * q_scale (they may be NULL there); the forward entries do not use the
+ * workspace (it may be NULL there).
  */
 typedef struct sage_quant {
   int8_t *q_codes;
