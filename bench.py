@@ -217,15 +217,16 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        sage.sage_quant_prep(qd, kd, vd, out=quant)
-        sage.sage_attn_fwd(quant, out=out)
-    torch.cuda.synchronize()
-    print("bench: warmup done, timing %d steps" % args.steps, file=sys.stderr, flush=True)
-
+    # everything the timed loop needs is set up before the warm-up, so that the
+    # GPU goes from the last warm-up step into the timed ones with no idle time
+    # in between (an idle card lowers its clock, and the first timed steps then
+    # ran up to 20% slower while it ramped back)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     clk = torch.zeros(2, sage.CLOCK_SAMPLES, 4, dtype=torch.int64, device=dev)
     sage.sage_clock_sample(clk[0], stream)       # first launch (code-object load) stays out of the timing
+    for _ in range(args.warmup):
+        sage.sage_quant_prep(qd, kd, vd, out=quant)
+        sage.sage_attn_fwd(quant, out=out)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     sage.sage_clock_sample(clk[0], stream)
@@ -238,6 +239,7 @@ def main():
     sage.sage_clock_sample(clk[1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    print("bench: timed %d steps after %d warm-up steps" % (args.steps, args.warmup), file=sys.stderr, flush=True)
     sclk = shader_clock_ghz(clk.cpu().numpy())
     step_ms = [e[0].elapsed_time(e[2]) for e in ev]
     prep_ms = [e[0].elapsed_time(e[1]) for e in ev]
@@ -266,6 +268,7 @@ def main():
         "step_ms_cv": statistics.pstdev(step_ms) / statistics.mean(step_ms),
         "step_ms_p10": statistics.quantiles(step_ms, n=10)[0] if len(step_ms) > 1 else step_ms[0],
         "step_ms_p90": statistics.quantiles(step_ms, n=10)[-1] if len(step_ms) > 1 else step_ms[0],
+        "step_ms_each": [round(x, 4) for x in step_ms],
         "prep_ms_p50": statistics.median(prep_ms),
         "fwd_ms_p50": statistics.median(fwd_ms),
         "fwd_tflops_p50": w.flops / (statistics.median(fwd_ms) * 1e-3) / 1e12,
