@@ -2,8 +2,6 @@
 shader-clock sample and the matrix-core peak sample that bench.py reports
 beside the nominal peak."""
 
-import time
-
 import pytest
 import torch
 
@@ -15,18 +13,23 @@ DEV = torch.device("cuda:0")
 
 
 def test_clock_sample_gives_a_plausible_clock_on_most_units():
+    """Two samples around busy matrix work on every SIMD (an idle unit may be
+    clock-gated, and its counter then barely moves)."""
     clk = torch.zeros(2, sage.CLOCK_SAMPLES, 4, dtype=torch.int64, device=DEV)
+    dst = torch.zeros(sage.PEAK_WORKGROUPS * 256, dtype=torch.int32, device=DEV)
+    sage.sage_mfma_peak_sample(0, 1, dst)
     sage.sage_clock_sample(clk[0])
     torch.cuda.synchronize()
-    time.sleep(0.05)
+    sage.sage_clock_sample(clk[0])
+    sage.sage_mfma_peak_sample(0, 4096, dst)
     sage.sage_clock_sample(clk[1])
     torch.cuda.synchronize()
     s = bench.shader_clock_ghz(clk.cpu().numpy())
     assert s is not None
-    print("  clock over an idle 50 ms: median %.3f GHz (%.3f-%.3f), %d units" % (s["median"], s["min"], s["max"],
-                                                                             s["units"]), flush=True)
+    print("  clock over a matrix-instruction stream: median %.3f GHz (%.3f-%.3f), %d units"
+          % (s["median"], s["min"], s["max"], s["units"]), flush=True)
     assert s["units"] >= 200                      # 256 compute units; 2048 workgroups reach nearly all
-    assert 0.05 < s["min"] <= s["median"] <= s["max"] < 3.0
+    assert 0.5 < s["min"] <= s["median"] <= s["max"] < 3.0
 
 
 @pytest.mark.parametrize("kind", [0, 1])
