@@ -166,3 +166,28 @@ def test_calls_with_preallocated_buffers_allocate_nothing(mode):
     torch.cuda.synchronize()
     assert torch.cuda.memory_stats(DEV)["allocation.all.allocated"] == before
     assert torch.equal(_bits(out), _bits(sage.sage_attention(q, k, v)))
+
+
+def test_two_streams_at_once_match_sequential_runs():
+    """The library keeps no per-call state: prep + forward of two independent
+    problems enqueued on two streams at the same time (default priority) give
+    the sequential results bit for bit (the three-launch prep; the single pass
+    must not share the device with other work, as its header says)."""
+    w = WORKLOADS["ragged_tails"]
+    a = [t.to(DEV) for t in make_inputs(w, seed=31, B=1, H=4, Nq=700, Nkv=900, D=128)]
+    b = [t.to(DEV) for t in make_inputs(w, seed=32, B=2, H=2, Nq=500, Nkv=1300, D=64)]
+    ref_a = sage.sage_attn_fwd(sage.sage_quant_prep(*a))
+    ref_b = sage.sage_attn_fwd(sage.sage_quant_prep(*b))
+    qa, qb = sage.sage_quant_prep(*a), sage.sage_quant_prep(*b)
+    oa, ob = torch.empty_like(ref_a), torch.empty_like(ref_b)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(5):
+        with torch.cuda.stream(sa):
+            sage.sage_quant_prep(*a, out=qa)
+            sage.sage_attn_fwd(qa, out=oa)
+        with torch.cuda.stream(sb):
+            sage.sage_quant_prep(*b, out=qb)
+            sage.sage_attn_fwd(qb, out=ob)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(oa), _bits(ref_a)) and torch.equal(_bits(ob), _bits(ref_b))
