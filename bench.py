@@ -273,7 +273,8 @@ def main():
         "dtype": "int8+fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nkv": w.Nkv, "D": w.D,
-                   "causal": False, "parallelism": "none (1 GPU)"},
+                   "causal": False, "seed": w.seed, "outlier_p": w.outlier_p,
+                   "parallelism": "none (1 GPU)"},
         "pct_of_peak": 100.0 * (w.flops / (ms_per_step * 1e-3) / 1e12) / MFMA_PEAK_TFLOPS,
         "step_ms_p50": statistics.median(step_ms),
         "step_ms_cv": statistics.pstdev(step_ms) / statistics.mean(step_ms),
