@@ -20,8 +20,9 @@
 //   (accumulated on a constant offset so that each score reads back as a
 //   float with one subtraction, see kScoreBias)
 //   softmax on S^T: every lane holds ONE query and 32 of the 64 keys, so the
-//   row max / row sum are in-lane reductions plus one permlane32 swap, and
-//   m, d, alpha are per-lane scalars
+//   row max is an in-lane reduction plus one permlane32 swap, m and alpha are
+//   per-lane scalars, and each half-wave carries the running row sum of its
+//   own 32 keys (the two halves are added once, after the last tile)
 //   P8^T stays in registers: the accumulator layout of S^T is already the
 //   B-operand layout of O^T = V^T . P^T (no LDS round trip for P)
 //   partial^T[D x 32] = V_j^T . P8^T         (D/32) v_mfma_f32_32x32x64_f8f6f4
@@ -72,14 +73,20 @@ template <int D> struct FwdOccupancy { static constexpr int waves_per_simd = D =
 // and the RO update fills the gaps.
 constexpr int kPrioMatrix = 3, kPrioExp = 2, kPrioScale = 1, kPrioUpdate = 0;
 
+// The lane id, computed afresh where it is used (v_mbcnt) so that no register
+// carries it through the traversal.  Volatile asm: the compiler would otherwise
+// hoist the computation out of the tile loop, or merge it with an earlier one,
+// and keep the result live across the loop.
+__device__ __forceinline__ int fresh_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Masking of the ragged last tile: lane l holds keys kb*32 + 8*(v/4) + 4*(l/32)
 // + v%4, so key (kb, v) is past Nkv iff kb*32 + 8*(v/4) + v%4 >= kvalid -
-// 4*(l/32).  The lane id is recomputed here (v_mbcnt) so that no register
-// carries it, or the 32 key indices, through the traversal.
-__device__ __forceinline__ int masked_key_limit(int kvalid) {
-  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  return kvalid - 4 * (lane >> 5);
-}
+// 4*(l/32).  No register carries the 32 key indices through the traversal.
+__device__ __forceinline__ int masked_key_limit(int kvalid) { return kvalid - 4 * (fresh_lane_id() >> 5); }
 
 // Scores accumulate on top of the bit pattern of 1/(2 pi), 0x3E22F983, which
 // the matrix instruction takes as an inline constant for its accumulator
@@ -150,7 +157,8 @@ __device__ __forceinline__ void issue_tile(uint8_t *dst, const int8_t *kg, const
 
 template <int D>
 struct FwdState {
-  float m, dsum;
+  float m;      // running row max (scaled, log2 units), the same in both half-waves
+  float dsum;   // running row sum over this half-wave's keys (x 448)
   v16f ro[D / 32];
 };
 
@@ -158,7 +166,7 @@ struct FwdState {
 // `cur` holds tile j; tile j+1 is copied into `nxt` meanwhile.  Ends with the
 // workgroup barrier that publishes `nxt` and retires `cur`.
 template <int D, bool CAP, bool RACE, int QPW>
-__device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, const v4i *qop, float sq, int j,
+__device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, const v4i *qop, float sq, float pinf, int j,
                                           const uint8_t *cur, uint8_t *nxt, const int8_t *kg, const uint8_t *vg,
                                           const float *ksc, int wave, int lane, int row) {
   constexpr int NS = D / 32;
@@ -204,21 +212,20 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   }
 
   // ---- online softmax; max in the integer domain (the per-tile factor is >= 0) ----
-  // 32 values -> 16 three-input maxima in a tree of depth 3 (+1 two-input)
-  int m10[11];
+  // 32 values -> 12 -> 4 -> 1: fifteen three-input maxima and one two-input
+  int m12[10];
 #pragma unroll
   for (int i = 0; i < 10; ++i) {
     const int x = 3 * i;
-    m10[i] = max(max(sacc[x >> 4][x & 15], sacc[(x + 1) >> 4][(x + 1) & 15]), sacc[(x + 2) >> 4][(x + 2) & 15]);
+    m12[i] = max(max(sacc[x >> 4][x & 15], sacc[(x + 1) >> 4][(x + 1) & 15]), sacc[(x + 2) >> 4][(x + 2) & 15]);
   }
-  m10[10] = max(sacc[1][14], sacc[1][15]);
-  const int m4a = max(max(m10[0], m10[1]), m10[2]), m4b = max(max(m10[3], m10[4]), m10[5]);
-  const int m4c = max(max(m10[6], m10[7]), m10[8]), m4d = max(m10[9], m10[10]);
+  const int m4a = max(max(m12[0], m12[1]), m12[2]), m4b = max(max(m12[3], m12[4]), m12[5]);
+  const int m4c = max(max(m12[6], m12[7]), m12[8]), m4d = max(max(m12[9], sacc[1][14]), sacc[1][15]);
   int mx = max(max(max(m4a, m4b), m4c), m4d);
   mx = partner_max(mx);
   const float c = (sq * load_uniform(ksc + j)) * p.sl2;   // fp32(fp32(sq * sk_j) * sl2)
   const float cu = c * kScoreUnit;                          // exact
-  const float mnew = __builtin_amdgcn_fmed3f(st.m, score_scaled(mx) * cu, INFINITY);   // max; no NaN here
+  const float mnew = __builtin_amdgcn_fmed3f(st.m, score_scaled(mx) * cu, pinf);   // max; no NaN here
   const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);   // "rescale"; 0 on the first tile
   const float nb = kLog2_448 - mnew;
   // arguments first (full rate), then the exps under the higher priority
@@ -247,9 +254,11 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
     const int kb = i >> 2, v0 = 4 * (i & 3);
     s8[i] = (pv[kb][v0] + pv[kb][v0 + 1]) + (pv[kb][v0 + 2] + pv[kb][v0 + 3]);
   }
-  float ls = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
-  ls = partner_sum(ls);
-  st.dsum = __builtin_fmaf(st.dsum, alpha, ls);      // d carries the factor 448
+  const float ls = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+  // this half-wave's running sum (d carries the factor 448); the halves meet
+  // after the last tile, which only reorders the FP32 additions of the row sum
+  st.dsum = __builtin_fmaf(st.dsum, alpha, ls);
+  asm volatile("" ::"v"(ls));   // kept live past the FMA, as the partials below
   st.m = mnew;
 
   // ---- P8 (E4M3FN, RNE) packed straight into the B operand of the PV product ----
@@ -272,10 +281,11 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
         const int v = 4 * (w & 3) + e;
         pc[(w >> 2) * 32 + 8 * (v >> 2) + 4 * hi + (v & 3)] = (uint8_t)((uint32_t)pop[w] >> (8 * e));
       }
+    const float dj = partner_sum(st.dsum);   // d after tile j: both halves
     if (hi == 0) {
       float *md = p.md_cap + (((size_t)blockIdx.x * kBQ + row) * T + j) * 3;
       md[0] = st.m;
-      md[1] = st.dsum;
+      md[1] = dj;
       md[2] = alpha;
     }
   }
@@ -297,6 +307,12 @@ __device__ __forceinline__ void tile_step(const FwdParams &p, FwdState<D> &st, c
   for (int cb = 0; cb < NS; ++cb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) st.ro[cb][v] = __builtin_fmaf(st.ro[cb][v], alpha, part[cb][v]);
+  // The partials stay live past their last FMA: where the addend dies at the
+  // FMA, the compiler writes the sum over it (v_fmac) and copies it back into
+  // the loop-carried register, one extra move per accumulator tuple and tile.
+#pragma unroll
+  for (int cb = 0; cb < NS; ++cb)
+    asm volatile("" ::"v"(part[cb].lo.lo), "v"(part[cb].lo.hi), "v"(part[cb].hi.lo), "v"(part[cb].hi.hi));
   if (CAP) {
     // lane (hi, row) holds channels 32 cb + 8 (v / 4) + 4 hi + v % 4
     const size_t o = (((size_t)blockIdx.x * kBQ + row) * T + j) * D;
@@ -411,16 +427,23 @@ __global__ __launch_bounds__(256 * QPW, FwdOccupancy<D>::waves_per_simd) void k_
   v4i qop[NS];
   float sq;
   if (QIN) {
-    // lds_b is first written by tile 0's step, after the barrier below
+    // lds_b is first written by tile 0's step, after the barrier below; the
+    // scale is the same in every lane and stays in a VGPR (as below)
     sq = quantize_q_operand<D>(p, bh, qb, wq, lane, (float *)lds_b, qop);
-    sq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sq)));   // uniform: keep it scalar
   } else {
     const int8_t *qsrc = p.q_codes + ((size_t)u * 4 + wq) * (NS * 1024) + lane * 16;
 #pragma unroll
     for (int s = 0; s < NS; ++s) qop[s] = *(const v4i *)(qsrc + s * 1024);
-    sq = load_uniform(p.q_scale + u);
+    // the Q scale in a VGPR: its per-tile product with the K scale (an SGPR)
+    // then needs no copy, as one VALU instruction reads at most one SGPR
+    asm volatile("v_mov_b32 %0, %1" : "=v"(sq) : "s"(load_uniform(p.q_scale + u)));
   }
   const int row = wq * 32 + (lane & 31);
+  // +inf as a value the compiler cannot fold: the running max then stays one
+  // v_med3_f32 (folded to a max, it costs one more instruction to canonicalize
+  // its loop-carried operand)
+  float pinf;
+  asm volatile("s_mov_b32 %0, 0x7f800000" : "=s"(pinf));
 
   FwdState<D> st;
   st.m = -INFINITY;
@@ -436,18 +459,18 @@ __global__ __launch_bounds__(256 * QPW, FwdOccupancy<D>::waves_per_simd) void k_
   for (int j = 0; j < T; ++j) {
     uint8_t *cur = (j & 1) ? lds_b : lds_a;
     uint8_t *nxt = (j & 1) ? lds_a : lds_b;
-    tile_step<D, CAP, RACE, QPW>(p, st, qop, sq, j, cur, nxt, kg, vg, ksc, wave, lane, row);
+    tile_step<D, CAP, RACE, QPW>(p, st, qop, sq, pinf, j, cur, nxt, kg, vg, ksc, wave, lane, row);
   }
 
   __builtin_amdgcn_s_setprio(3);                 // finish and free the slot quickly
 
   // ---- final conversion: reciprocal of d, per-channel V scale, BF16 ----
-  // lane and row recomputed (v_mbcnt, scalar wave index) so that no register
-  // holds them through the traversal
-  const int elane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  // lane and row recomputed (scalar wave index) so that no register holds them
+  // through the traversal
+  const int elane = fresh_lane_id();
   const int hi = elane >> 5;
   const int n = qb * kBQ + wq * 32 + (elane & 31);
-  const float r = 1.0f / st.dsum;                 // "reciprocal" (d includes the 448)
+  const float r = 1.0f / partner_sum(st.dsum);    // "reciprocal" of both halves' d (includes the 448)
   if (CAP && hi == 0) p.r_cap[(size_t)blockIdx.x * kBQ + wq * 32 + (elane & 31)] = r;
   if (live && n < p.Nq) {
     const int b = bh / p.H, h = bh - b * p.H;
