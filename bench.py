@@ -83,6 +83,27 @@ def shader_clock_ghz(samples):
             "units": len(set((int(r[2]), (int(r[3]) >> 8) & 0x7F) for r in samples[1]))}
 
 
+def valu_rates(words, mix):
+    """Cycles per instruction that each SIMD retired for every active role of
+    the vector-issue sample `mix` (words: [VALU_WORKGROUPS, 16, 3] int of
+    rounds, cycles, result word): per SIMD, the role's waves' instructions per
+    cycle are summed; median over the SIMDs of the device."""
+    import numpy as np
+    from quantized_exact_attention_amd import sage
+    roles = sage.VALU_MIXES[mix]
+    w = np.asarray(words, dtype=np.float64).reshape(-1, 16, 3)
+    out = {}
+    for r in sorted(set(roles) - {0}):
+        per_simd = []
+        for simd in range(4):
+            waves = [simd + 4 * g for g in range(4) if roles[g] == r]
+            ipc = sum(w[:, i, 0] * sage.VALU_ROUND_INSTRUCTIONS[r] / np.maximum(w[:, i, 1], 1.0) for i in waves)
+            per_simd.append(ipc)
+        ipc = np.concatenate(per_simd)
+        out[{1: "fma", 2: "exp", 3: "matrix"}[r]] = float(np.median(1.0 / ipc))
+    return out
+
+
 def _oracle_blocks(args):
     """Worker: time the oracle's attention over the given 128-row Q blocks of
     one head (single-threaded numpy in its own process)."""
@@ -390,6 +411,24 @@ def main():
     peak["unit"] = "TOP/s"
     peak["fwd_frac_of_measured"] = achieved / (0.5 * (peak["int8_tops"] + peak["fp8_tops"]))
     res["mfma_peak_measured"] = peak
+    # Vector issue rates on this device (cycles per wave64 instruction per
+    # SIMD): FP32 FMA from one, three and four waves, exp from three waves, and
+    # both beside a matrix-instruction stream on the same SIMD; the inputs of
+    # the forward's per-wave-tile cycle account
+    vdst = torch.empty(3 * 16 * sage.VALU_WORKGROUPS, dtype=torch.int32, device=dev)
+    sage.sage_valu_sample(0, 1, vdst, stream)
+    torch.cuda.synchronize()
+    vr = {}
+    for mix, name in ((0, "fma_1wave"), (1, "fma_3waves"), (2, "fma_4waves"), (3, "exp_3waves"),
+                      (4, "fma_3waves_beside_matrix"), (5, "exp_3waves_beside_matrix")):
+        sage.sage_valu_sample(mix, 200, vdst, stream)
+        torch.cuda.synchronize()
+        r = valu_rates(vdst.view(sage.VALU_WORKGROUPS, 16, 3).cpu().numpy(), mix)
+        vr[name] = r["exp" if "exp" in name else "fma"]
+        if "matrix" in r:                        # the matrix stream's own rate beside that work
+            vr["matrix_beside_" + name.split("_")[0]] = r["matrix"]
+    vr["unit"] = "shader-clock cycles per instruction per SIMD"
+    res["valu_rates_measured"] = vr
     if w.name == "single_tile":
         # the pages quote this fixture's forward both batched and as single
         # launches (2,000 samples); time single launches the same way: one

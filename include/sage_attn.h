@@ -325,6 +325,31 @@ int sage_clock_sample(uint64_t *dst, void *stream);
 #define SAGE_PEAK_MAX_ITERS 65536
 int sage_mfma_peak_sample(int kind, int iters, uint32_t *dst, void *stream);
 
+/* Diagnostics: a sample of the vector issue rates that bound the forward's
+ * softmax work, alone and beside matrix work, for the per-wave-tile cycle
+ * account of the forward.  SAGE_VALU_WORKGROUPS workgroups of sixteen waves
+ * (one per compute unit of a 256-CU device; wave w runs on SIMD w % 4); the
+ * four waves of each SIMD take the roles of `mix` (role 0 idle, 1 FP32 FMA
+ * v_fma_f32 with sixteen independent chains, 2 v_exp_f32, 3 the INT8
+ * 32x32x32 matrix instruction in four independent accumulation chains):
+ *   mix 0 = {1,0,0,0}  one FMA wave per SIMD
+ *   mix 1 = {1,1,1,0}  three FMA waves
+ *   mix 2 = {1,1,1,1}  four FMA waves
+ *   mix 3 = {2,2,2,0}  three exp waves
+ *   mix 4 = {3,1,1,1}  a matrix stream beside three FMA waves
+ *   mix 5 = {3,2,2,2}  a matrix stream beside three exp waves
+ * Every active wave issues rounds of 64 vector (or 16 matrix) instructions
+ * until window_kcycles * 1000 shader-clock cycles have passed, then writes
+ * dst[3 * (16 * workgroup + wave) + {0, 1, 2}] = {rounds completed (0 for idle
+ * waves), cycles taken (s_memtime), a word of its results}; dst: device uint32
+ * of 3 * 16 * SAGE_VALU_WORKGROUPS elements, 4-byte aligned, caller-owned.
+ * SAGE_E_ARG for a mix outside [0, SAGE_VALU_MIXES) or window_kcycles outside
+ * [1, SAGE_VALU_MAX_KCYCLES]. */
+#define SAGE_VALU_WORKGROUPS 256
+#define SAGE_VALU_MIXES 6
+#define SAGE_VALU_MAX_KCYCLES 10000
+int sage_valu_sample(int mix, int window_kcycles, uint32_t *dst, void *stream);
+
 /* SAGE_OK if `device` is a gfx950 GPU, else SAGE_E_DEVICE (one HIP query). */
 int sage_device_check(int device);
 

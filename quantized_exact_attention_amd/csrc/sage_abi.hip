@@ -239,6 +239,84 @@ __global__ __launch_bounds__(256) void k_mfma_peak(int iters, uint32_t *dst) {
   dst[(size_t)blockIdx.x * 256 + threadIdx.x] = word;
 }
 
+
+// Vector-issue sample.  One workgroup of sixteen waves per compute unit; wave
+// w runs on SIMD w % 4 and takes role kValuMix[mix][w / 4]: 0 idle, 1 FP32 FMA
+// (v_fma_f32, sixteen independent chains), 2 v_exp_f32 (sixteen independent),
+// 3 v_mfma_i32_32x32x32_i8 (four independent accumulation chains).  Every
+// active wave issues its stream for `window` shader-clock cycles (checked once
+// per 64 vector or 16 matrix instructions) and records how many such rounds it
+// completed and the cycles it took, so the instructions each SIMD retired per
+// cycle follow for every role, alone and beside a matrix-instruction stream.
+constexpr int kValuMix[SAGE_VALU_MIXES][4] = {
+    {1, 0, 0, 0}, {1, 1, 1, 0}, {1, 1, 1, 1}, {2, 2, 2, 0}, {3, 1, 1, 1}, {3, 2, 2, 2},
+};
+
+#define SAGE_FMA16                                                                                     \
+  _Pragma("unroll") for (int i = 0; i < 16; ++i) asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc[i]) \
+                                                              : "v"(x), "v"(y));
+#define SAGE_EXP16 _Pragma("unroll") for (int i = 0; i < 16; ++i) asm volatile("v_exp_f32 %0, %0" : "+v"(acc[i]));
+
+__global__ __launch_bounds__(1024) void k_valu_sample(int mix, uint64_t window, uint32_t *dst) {
+  // 96 KiB of LDS: more than half of a compute unit's, so each workgroup gets a unit of its own
+  __shared__ uint32_t pin[24 * 1024];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) pin[blockIdx.x % (24 * 1024)] = (uint32_t)mix;
+  const int role = kValuMix[mix][wave >> 2];
+  uint32_t rounds = 0;
+  uint32_t word = 0;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = (float)(i + lane) * 0x1p-8f;
+  const float x = 1.0f, y = (float)lane * 0x1p-20f;
+  __syncthreads();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  if (role == 1) {
+    for (;;) {
+      const uint64_t t = __builtin_amdgcn_s_memtime();
+      SAGE_FMA16 SAGE_FMA16 SAGE_FMA16 SAGE_FMA16
+      ++rounds;
+      if (t - t0 >= window) break;
+    }
+  } else if (role == 2) {
+    // exp2 of exp2 grows to +inf within a few rounds and stays there; the
+    // instruction's issue cost does not depend on the value
+    for (;;) {
+      const uint64_t t = __builtin_amdgcn_s_memtime();
+      SAGE_EXP16 SAGE_EXP16 SAGE_EXP16 SAGE_EXP16
+      ++rounds;
+      if (t - t0 >= window) break;
+    }
+  } else if (role == 3) {
+    const v4i a = {lane, lane * 3, lane * 5, lane * 7}, b = {lane * 11, lane * 13, 17, 19};
+    v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (;;) {
+      const uint64_t t = __builtin_amdgcn_s_memtime();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c3, 0, 0, 0);
+      }
+      ++rounds;
+      if (t - t0 >= window) break;
+    }
+    word = (uint32_t)(c0[lane & 15] ^ c1[3] ^ c2[7] ^ c3[15]);
+  }
+  const uint64_t cycles = __builtin_amdgcn_s_memtime() - t0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) word ^= __float_as_uint(acc[i]);
+  if (lane == 0) {
+    uint32_t *d = dst + ((size_t)blockIdx.x * 16 + wave) * 3;
+    d[0] = role == 0 ? 0u : rounds;
+    d[1] = (uint32_t)min(cycles, (uint64_t)0xffffffffu);
+    d[2] = word ^ pin[(blockIdx.x + 1) % (24 * 1024)];
+  }
+}
+#undef SAGE_FMA16
+#undef SAGE_EXP16
+
 }  // namespace
 
 extern "C" {
@@ -253,6 +331,18 @@ int sage_mfma_peak_sample(int kind, int iters, uint32_t *dst, void *stream) {
     hipLaunchKernelGGL(k_mfma_peak<0>, dim3(SAGE_PEAK_WORKGROUPS), dim3(256), 0, (hipStream_t)stream, iters, dst);
   else
     hipLaunchKernelGGL(k_mfma_peak<1>, dim3(SAGE_PEAK_WORKGROUPS), dim3(256), 0, (hipStream_t)stream, iters, dst);
+  return hipGetLastError() == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
+}
+
+int sage_valu_sample(int mix, int window_kcycles, uint32_t *dst, void *stream) {
+  if (!dst) return SAGE_E_NULL;
+  if (((uintptr_t)dst & 3u) != 0) return SAGE_E_ALIGN;
+  if (mix < 0 || mix >= SAGE_VALU_MIXES || window_kcycles < 1 || window_kcycles > SAGE_VALU_MAX_KCYCLES)
+    return SAGE_E_ARG;
+  int r = device_ok();
+  if (r) return r;
+  hipLaunchKernelGGL(k_valu_sample, dim3(SAGE_VALU_WORKGROUPS), dim3(1024), 0, (hipStream_t)stream, mix,
+                     (uint64_t)window_kcycles * 1000u, dst);
   return hipGetLastError() == hipSuccess ? SAGE_OK : SAGE_E_LAUNCH;
 }
 

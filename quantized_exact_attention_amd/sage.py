@@ -77,12 +77,14 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(SageStrides), vp]
         L.sage_clock_sample.argtypes = [vp, vp]
         L.sage_mfma_peak_sample.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+        L.sage_valu_sample.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
         L.sage_device_check.argtypes = [ctypes.c_int]
         L.sage_status_string.argtypes = [ctypes.c_int]
         L.sage_status_string.restype = ctypes.c_char_p
         for name in ("sage_buffer_bytes", "sage_prep_status_offset", "sage_quant_prep",
                      "sage_quant_prep_single_pass", "sage_attn_fwd", "sage_attn_fwd_paired", "sage_attn_fwd_capture",
-                     "sage_device_check", "sage_clock_sample", "sage_mfma_peak_sample", "sage_quant_prep_kv",
+                     "sage_device_check", "sage_clock_sample", "sage_mfma_peak_sample", "sage_valu_sample",
+                     "sage_quant_prep_kv",
                      "sage_attn_fwd_q"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -400,3 +402,23 @@ def sage_mfma_peak_sample(kind: int, iters: int, dst: torch.Tensor, stream=None)
     _check(lib().sage_mfma_peak_sample(kind, iters, dst.data_ptr(), _stream_handle(stream, dst.device)),
            "sage_mfma_peak_sample")
     return PEAK_WORKGROUPS * 4 * iters * 4 * PEAK_OPS_PER_INSTRUCTION[kind]
+
+
+VALU_WORKGROUPS = 256
+VALU_MAX_KCYCLES = 10000
+# roles of the four waves of each SIMD per mix: 0 idle, 1 FP32 FMA, 2 exp,
+# 3 INT8 matrix instruction; instructions per round of each role
+VALU_MIXES = {0: (1, 0, 0, 0), 1: (1, 1, 1, 0), 2: (1, 1, 1, 1), 3: (2, 2, 2, 0), 4: (3, 1, 1, 1), 5: (3, 2, 2, 2)}
+VALU_ROUND_INSTRUCTIONS = {1: 64, 2: 64, 3: 16}
+
+
+def sage_valu_sample(mix: int, window_kcycles: int, dst: torch.Tensor, stream=None) -> None:
+    """Launch the vector-issue sample `mix` (see VALU_MIXES) for about
+    window_kcycles * 1000 shader-clock cycles on `stream`; dst: contiguous
+    int32 CUDA tensor of 3 * 16 * VALU_WORKGROUPS elements, per wave (rounds
+    completed, cycles taken, a result word)."""
+    if dst.dtype != torch.int32 or dst.numel() < 3 * 16 * VALU_WORKGROUPS or not dst.is_cuda or \
+            not dst.is_contiguous():
+        raise ValueError("dst must be a contiguous int32 CUDA tensor of %d elements" % (3 * 16 * VALU_WORKGROUPS))
+    _check(lib().sage_valu_sample(mix, window_kcycles, dst.data_ptr(), _stream_handle(stream, dst.device)),
+           "sage_valu_sample")

@@ -220,6 +220,16 @@ def test_mfma_peak_sample_validation_before_any_hip_call(L, no_gfx950):
     assert f(1, 65536, dst, None) in (0, -6, -7)
 
 
+def test_valu_sample_validation_before_any_hip_call(L, no_gfx950):
+    f = L.sage_valu_sample
+    dst = 1 << 44
+    assert f(0, 16, None, None) == -1
+    assert f(0, 16, dst + 2, None) == -4
+    for mix, kc in ((6, 16), (-1, 16), (0, 0), (5, -5), (1, 10001)):
+        assert f(mix, kc, dst, None) == -8, (mix, kc)
+    assert f(5, 10000, dst, None) in (0, -6, -7)
+
+
 def test_kv_prep_validation_before_any_hip_call(L, no_gfx950):
     """The K/V-only prep takes no q and accepts NULL Q codes and scale."""
     f = L.sage_quant_prep_kv

@@ -51,3 +51,27 @@ def test_mfma_peak_sample_runs_near_the_matrix_peak(kind):
     assert 2500 < rate < 5200
     with pytest.raises(sage.SageError):
         sage.sage_mfma_peak_sample(2, 16, dst)
+
+
+def test_valu_sample_rates_are_ordered_as_the_issue_model_says():
+    """More issuing waves retire more FMAs per cycle; exp costs more than FMA;
+    a matrix-instruction stream on the same SIMD slows the vector work."""
+    dst = torch.zeros(3 * 16 * sage.VALU_WORKGROUPS, dtype=torch.int32, device=DEV)
+    rates = {}
+    for mix in range(len(sage.VALU_MIXES)):
+        sage.sage_valu_sample(mix, 100, dst)
+        torch.cuda.synchronize()
+        words = dst.view(sage.VALU_WORKGROUPS, 16, 3).cpu().numpy()
+        roles = sage.VALU_MIXES[mix]
+        for g, role in enumerate(roles):          # idle waves report 0 rounds, active ones at least one
+            rounds = words[:, 4 * g:4 * g + 4, 0]
+            assert (rounds == 0).all() if role == 0 else (rounds >= 1).all(), (mix, g)
+        rates[mix] = bench.valu_rates(words, mix)
+        print("  mix %d %s: %s" % (mix, roles, {k: round(v, 2) for k, v in rates[mix].items()}), flush=True)
+    fma1, fma3, fma4, exp3 = rates[0]["fma"], rates[1]["fma"], rates[2]["fma"], rates[3]["exp"]
+    assert 1.0 < fma4 <= fma3 * 1.05 and fma3 < fma1 < 20.0
+    assert fma3 < exp3 < 30.0
+    assert rates[4]["fma"] > fma3 and rates[5]["exp"] > exp3
+    assert 20.0 < rates[4]["matrix"] < 80.0
+    with pytest.raises(sage.SageError):
+        sage.sage_valu_sample(len(sage.VALU_MIXES), 10, dst)
