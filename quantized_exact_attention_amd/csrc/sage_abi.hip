@@ -311,7 +311,7 @@ __global__ __launch_bounds__(1024) void k_valu_sample(int mix, uint64_t window, 
     uint32_t *d = dst + ((size_t)blockIdx.x * 16 + wave) * 3;
     d[0] = role == 0 ? 0u : rounds;
     d[1] = (uint32_t)min(cycles, (uint64_t)0xffffffffu);
-    d[2] = word ^ pin[(blockIdx.x + 1) % (24 * 1024)];
+    d[2] = word ^ pin[blockIdx.x % (24 * 1024)];   // written by thread 0 before the first barrier
   }
 }
 #undef SAGE_FMA16
