@@ -443,6 +443,20 @@ def main():
             single.append(a.elapsed_time(b))
         res["fwd_single_launch"] = {"samples": len(single), "p50_ms": statistics.median(single),
                                     "cv": statistics.pstdev(single) / statistics.mean(single)}
+        # and back to back: 20 batches of 100 forwards with no synchronization
+        # inside a batch, events around each batch; time per forward
+        batches = []
+        for _ in range(20):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(100):
+                sage.sage_attn_fwd(quant, out=out)
+            b.record(stream)
+            torch.cuda.synchronize()
+            batches.append(a.elapsed_time(b) / 100)
+        res["fwd_back_to_back"] = {"batches": len(batches), "launches_per_batch": 100,
+                                   "p50_ms": statistics.median(batches),
+                                   "cv": statistics.pstdev(batches) / statistics.mean(batches)}
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
