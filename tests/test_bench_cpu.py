@@ -1,5 +1,5 @@
-"""bench.py's host-side logic, no GPU: the one-GPU refusal and the clock
-computation from two counter samples."""
+"""bench.py's host-side logic, no GPU: the one-GPU refusal, the clock
+computation from two counter samples and the vector-issue rates."""
 
 import os
 import subprocess
@@ -35,3 +35,21 @@ def test_shader_clock_from_two_samples():
     assert s["units"] == n
     assert abs(s["min"] - 2.0) < 1e-9 and abs(s["max"] - 2.15) < 1e-9
     assert abs(s["median"] - np.median([2.0 + 0.01 * i for i in range(n)])) < 1e-9
+
+
+def test_valu_rates_sum_the_waves_of_a_role_per_simd():
+    """Per SIMD, a role's instructions per cycle are the sum over its waves;
+    the cycles per instruction reported is the median over SIMDs."""
+    from quantized_exact_attention_amd import sage
+    mix = 4                                       # {matrix, FMA, FMA, FMA}
+    words = np.zeros((sage.VALU_WORKGROUPS, 16, 3), np.int64)
+    for g in range(sage.VALU_WORKGROUPS):
+        for w in range(16):
+            role = sage.VALU_MIXES[mix][w // 4]
+            words[g, w, 1] = 100000               # cycles
+            # each FMA wave retires one instruction per 15 cycles: 3 waves -> 5 cycles each
+            words[g, w, 0] = 100000 // (15 * 64) if role == 1 else 100000 // (40 * 16)
+    r = bench.valu_rates(words, mix)
+    assert abs(r["fma"] - 100000 / (3 * (100000 // (15 * 64)) * 64)) < 1e-9
+    assert abs(r["matrix"] - 100000 / ((100000 // (40 * 16)) * 16)) < 1e-9
+    assert bench.valu_rates(words, 0).keys() == {"fma"}
